@@ -1,0 +1,165 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) MLA paged-KV decode library, libmla.so.
+ *
+ * Multi-head latent attention (MLA) decoding: every query row of 576 dims
+ * (512 latent "NoPE" dims followed by 64 RoPE dims) attends over one shared
+ * latent KV row per token; the first 512 dims of that row also serve as V.
+ * Tokens live in 64-token pages of a shared pool, found through a per-
+ * sequence block table.  Sources: geoz.com.cn "FlashMLA: DeepSeek's
+ * high-performance decoding kernel for Hopper GPUs" (Introduction: MLA
+ * decoding over a paged KV cache for variable-length sequences);
+ * topnet.top "Was ist FlashMLA?" (Hauptmerkmale: BF16, page size 64;
+ * "MLA-Metadaten abrufen" and "MLA-Decodierung ausfuehren": the two-call
+ * interface, metadata computed once and reused by every layer, output plus
+ * log-sum-exp, causal flag); sao.pub FlashMLA overview (二、核心功能与架构:
+ * sparse `indices` and the FP8 cache row of 512 FP8 NoPE values, 4 FP32
+ * scales and 64 BF16 RoPE values).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers of the current HIP device,
+ *     owned by the caller.  The library allocates no device memory and keeps
+ *     no per-call state; it caches only the device's compute-unit count.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; nothing synchronises.
+ *   - Every function returns an mla_status.  Host-checkable problems are
+ *     reported before anything is launched; nothing aborts or throws.  The
+ *     message for the last non-OK status of the calling thread is returned
+ *     by mla_last_error().
+ *   - Values inside device buffers are not validated on the hot path:
+ *     sparse indices outside [0, window) are masked (treated as absent);
+ *     block_table entries for needed blocks must lie in [0, num_pages).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARGUMENT = -1,   /* null pointer, bad size or mismatch */
+    MLA_ERR_UNSUPPORTED = -2,        /* h_kv != 1, dims != 576/512, page != 64 */
+    MLA_ERR_WORKSPACE_TOO_SMALL = -3,
+    MLA_ERR_HIP = -4                 /* a HIP runtime call or launch failed */
+} mla_status;
+
+typedef enum {
+    /* [num_pages, 64, 1, 576] bf16, one 1152-byte row per token */
+    MLA_KV_BF16 = 0,
+    /* [num_pages, 64, 1, 656] bytes per token: 512 e4m3fn NoPE codes, then
+     * 4 little-endian fp32 scales (scale g applies to NoPE dims
+     * [128g, 128g+128)), then 64 little-endian bf16 RoPE values */
+    MLA_KV_FP8_656 = 1
+} mla_kv_format;
+
+/* Arguments of one decode call (one layer). */
+typedef struct {
+    int batch;               /* number of sequences b */
+    int s_q;                 /* query tokens per sequence (>= 1) */
+    int h_q;                 /* query heads */
+    int h_kv;                /* KV heads; must be 1 */
+    int d_qk;                /* must be 576 */
+    int d_v;                 /* must be 512 (the "dv" argument of the pages) */
+    int page_size;           /* must be 64 */
+    int num_pages;           /* pages in the pool */
+    int max_blocks_per_seq;  /* row stride of block_table, in elements */
+    int topk;                /* 0: dense; > 0: indices is [batch, s_q, topk] */
+    int kv_format;           /* an mla_kv_format */
+    float softmax_scale;     /* multiplies q.k; the usual value is 576^-0.5 */
+    int causal;              /* 1: query s of s_q sees the first
+                                L - s_q + 1 + s keys (clamped to [0, L]) */
+    int num_parts;           /* the value mla_metadata_size returned (or the
+                                one passed to mla_get_metadata) */
+    const void *q;           /* [batch, s_q, h_q, 576] bf16, contiguous */
+    const void *kcache;      /* page pool, layout per kv_format */
+    const int32_t *block_table;    /* [batch, max_blocks_per_seq]; entry j is
+                                      the pool page of tokens [64j, 64j+64) */
+    const int32_t *cache_seqlens;  /* [batch], L_b >= 0 */
+    const int32_t *indices;        /* NULL, or [batch, s_q, topk] logical
+                                      token positions; -1 / out of range =
+                                      masked */
+    const int32_t *tile_metadata;  /* from mla_get_metadata */
+    const int32_t *num_splits;     /* from mla_get_metadata */
+    void *workspace;               /* scratch for split partials */
+    size_t workspace_bytes;
+    void *out;               /* [batch, s_q, h_q, 512] bf16 (written) */
+    float *lse;              /* [batch, s_q, h_q] fp32 natural-log
+                                log-sum-exp of the scaled scores (written);
+                                -inf and out = 0 where no key is visible */
+} mla_decode_args;
+
+/*
+ * Sizes of the schedule arrays (topnet.top "Was ist FlashMLA?",
+ * "MLA-Metadaten abrufen": get_mla_metadata(cache_seqlens,
+ * s_q * h_q // h_kv, h_kv) returns tile_scheduler_metadata and num_splits).
+ *
+ *   q_rows_per_kv_head = s_q * h_q / h_kv; topk = 0 for dense.
+ *   *num_parts (out): the part count the library picks for this device and
+ *                     row count (a multiple of 8).
+ *   *tile_metadata_elems, *num_splits_elems (out): int32 element counts to
+ *     allocate, for the picked part count.  Use
+ *     mla_metadata_size_for_parts to size for a forced count.
+ */
+int mla_metadata_size(int batch, int s_q, int q_rows_per_kv_head, int h_kv, int topk,
+                      int *num_parts, size_t *tile_metadata_elems, size_t *num_splits_elems);
+
+/* Same sizes for an explicit part count (num_parts >= 1). */
+int mla_metadata_size_for_parts(int batch, int s_q, int topk, int num_parts,
+                                size_t *tile_metadata_elems, size_t *num_splits_elems);
+
+/*
+ * Build the split-KV schedule on the device (same passage as above).
+ *
+ *   cache_seqlens [batch] int32 (device); indices NULL (dense) or
+ *   [batch, s_q, topk] int32 (device).
+ *   num_parts: normally the value mla_metadata_size returned; any value
+ *   >= 1 gives a valid (if slower) schedule and must then be passed to the
+ *   decode unchanged.
+ *   tile_metadata, num_splits: device int32 arrays of the sizes above
+ *   (written).  Layout of tile_metadata:
+ *     [0..7]   header {num_parts, T, c0, units, total_blocks, 0x4D4C4131, 0, 0}
+ *     [8 + 8p .. 8 + 8p + 7] part p: {u_first, j_first, u_last, j_end,
+ *              split index of u_first, 0, 0, 0}; an empty part has u_first -1
+ *     [8 + 8P + u] blocks of 64 keys that unit u spans
+ *   where a unit is a sequence (dense) or a (sequence, query token) pair
+ *   (sparse).  num_splits[u+1] - num_splits[u] is the number of parts unit u
+ *   is spread over (num_splits[0] = 0).
+ * The result depends only on cache_seqlens (and indices); compute it once
+ * per decode step and reuse it for every layer.
+ */
+int mla_get_metadata(const int32_t *cache_seqlens, const int32_t *indices, int batch, int s_q,
+                     int q_rows_per_kv_head, int h_kv, int topk, int num_parts,
+                     int32_t *tile_metadata, int32_t *num_splits, void *stream);
+
+/* Bytes of device workspace mla_decode_kvcache needs for these arguments
+ * (fp32 partial outputs and partial log-sum-exps of split sequences). */
+int mla_workspace_size(const mla_decode_args *args, size_t *bytes);
+
+/*
+ * Decode one layer: out and lse for every (sequence, query token, head)
+ * (topnet.top "Was ist FlashMLA?", "MLA-Decodierung ausfuehren":
+ * flash_mla_with_kvcache(q, kvcache, block_table, cache_seqlens, dv,
+ * tile_scheduler_metadata, num_splits, causal) -> (o, lse); sao.pub,
+ * 二、核心功能与架构: with `indices`, only the listed tokens are attended).
+ *
+ * Enqueues the split-KV attention kernel and the log-sum-exp combine kernel
+ * on `stream`.  The metadata must come from mla_get_metadata with the same
+ * batch, s_q, h_q * s_q, topk, cache_seqlens, indices and num_parts.
+ */
+int mla_decode_kvcache(const mla_decode_args *args, void *stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *mla_last_error(void);
+
+/* Library ABI version (increments on incompatible changes). */
+int mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,72 @@
+// Device-side constants, vector types and small helpers shared by the
+// gfx950 (CDNA4) kernels of the MLA paged-KV decode library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Geometry fixed by the method: 64-token pages (topnet.top "Was ist
+// FlashMLA?", Hauptmerkmale), 576-dim query/key rows of 512 latent NoPE dims
+// plus 64 RoPE dims, V = the first 512 dims, and the 656-byte FP8 row of
+// 512 e4m3 codes, 4 fp32 scales and 64 bf16 RoPE values (sao.pub FlashMLA
+// overview, 二、核心功能与架构).
+constexpr int kPage = 64;
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kDnope = 512;
+constexpr int kBf16RowBytes = 2 * kDqk;  // 1152
+constexpr int kFp8RowBytes = 656;
+constexpr int kFp8ScaleOff = 512;
+constexpr int kFp8RopeOff = 528;
+
+// Schedule array layout (tile_metadata).
+constexpr int kHeader = 8;
+constexpr int kPartRow = 8;
+constexpr int kMagic = 0x4D4C4131;
+constexpr int kUnitOverhead = 2;  // c0: cost of one (unit, part) piece, in blocks
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// 2^x via v_exp_f32; exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) via v_log_f32.
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+}  // namespace mla

@@ -1,0 +1,40 @@
+// Internal interface between the C ABI (mla_api.cpp) and the kernel
+// launchers (mla_metadata.hip, mla_decode.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeParams {
+  const uint8_t* q;            // bf16 [units*R, 576]
+  const uint8_t* kcache;       // page pool
+  const int32_t* block_table;  // [batch, max_blocks]
+  const int32_t* seqlens;      // [batch]
+  const int32_t* indices;      // [batch, s_q, topk] or null
+  const int32_t* md;           // tile_metadata
+  const int32_t* num_splits;   // [units + 1]
+  uint16_t* out;               // bf16 [units*R, 512]
+  float* lse;                  // [units*R]
+  float* ws_o;                 // [slots, R, 512]
+  float* ws_lse;               // [slots, R]
+  int batch, s_q, h_q;
+  int R;                       // query rows per unit
+  int units;
+  int max_blocks, topk, num_parts, row_tiles;
+  int causal;
+  float scale_log2;            // softmax_scale * log2(e)
+};
+
+// Rows one decode workgroup covers for a given number of rows per unit.
+int rows_per_workgroup(int rows_per_unit);
+
+hipError_t launch_unit_blocks(const int32_t* seqlens, const int32_t* indices, int batch, int s_q,
+                              int topk, int units, int32_t* unit_blocks, hipStream_t stream);
+hipError_t launch_schedule(int units, int num_parts, int32_t* md, int32_t* num_splits,
+                           hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int kv_format, hipStream_t stream);
+
+}  // namespace mla

@@ -22,11 +22,12 @@ the schedule this project defines for them:
     part floor(position / T).
 
 The device arrays:
-  tile_metadata = header[8] + P rows of 8 int32
+  tile_metadata = header[8] + P rows of 8 int32 + U int32
     header = [P, T, c0, U, total_blocks, 0x4D4C4131, 0, 0]
     row p  = [u_first, j_first, u_last, j_end, split_of_u_first, 0, 0, 0]
              (j_end is one past the last block of u_last in the part;
               an empty part is [-1, 0, -1, 0, 0, 0, 0, 0])
+    then n_u for every unit
   num_splits = U + 1 int32 prefix sums of k_u, the number of parts unit u
                is spread over.
 """
@@ -86,7 +87,8 @@ def schedule(n_blocks, num_parts: int, c0: int):
     for u in range(U):
         num_splits[u + 1] = num_splits[u] + len(parts_of_unit[u])
 
-    md = np.zeros(HEADER + ROW * P, dtype=np.int32)
+    md = np.zeros(HEADER + ROW * P + U, dtype=np.int32)
+    md[HEADER + ROW * P:] = n_blocks
     md[:HEADER] = [P, T, c0, U, sum(n_blocks), MAGIC, 0, 0]
     for p in range(P):
         r = md[HEADER + ROW * p: HEADER + ROW * (p + 1)]
@@ -106,6 +108,7 @@ def check_schedule(md, num_splits, n_blocks):
     num_splits agree.  Raises AssertionError on a violation."""
     P, T, c0, U, total, magic = (int(v) for v in md[:6])
     assert magic == MAGIC and U == len(n_blocks) and total == int(sum(n_blocks))
+    assert list(md[HEADER + ROW * P:]) == [int(x) for x in n_blocks]
     cover = {}
     split_seen = {}
     last = (-1, -1)

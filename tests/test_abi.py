@@ -1,0 +1,116 @@
+"""C-ABI checks that need no GPU: the library loads, exports exactly what
+include/mla.h declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(mla_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mla_paged_kv_metadata_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmla.so is not built (python -m mla_paged_kv_metadata_amd.build)")
+    return _lib.load()
+
+
+def test_header_declares_expected_entry_points():
+    from mla_paged_kv_metadata_amd import _lib
+    assert declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from mla_paged_kv_metadata_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mla_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing else of ours leaks out
+    assert exported == set(declared_functions())
+
+
+def test_version(lib):
+    assert lib.mla_version() == 1
+
+
+def test_metadata_size_for_parts(lib):
+    md = ctypes.c_size_t()
+    ns = ctypes.c_size_t()
+    assert lib.mla_metadata_size_for_parts(64, 1, 0, 256, ctypes.byref(md), ctypes.byref(ns)) == 0
+    assert md.value == 8 + 8 * 256 + 64 and ns.value == 65
+    # sparse: one unit per (sequence, query token)
+    assert lib.mla_metadata_size_for_parts(4, 3, 16, 8, ctypes.byref(md), ctypes.byref(ns)) == 0
+    assert md.value == 8 + 64 + 12 and ns.value == 13
+    assert lib.mla_metadata_size_for_parts(-1, 1, 0, 8, ctypes.byref(md), ctypes.byref(ns)) == -1
+    assert lib.mla_metadata_size_for_parts(1, 1, 0, 0, ctypes.byref(md), ctypes.byref(ns)) == -1
+    assert b"num_parts" in lib.mla_last_error()
+
+
+def _args(**kw):
+    from mla_paged_kv_metadata_amd import _lib
+    a = _lib.MlaDecodeArgs()
+    a.batch, a.s_q, a.h_q, a.h_kv = 2, 1, 16, 1
+    a.d_qk, a.d_v, a.page_size = 576, 512, 64
+    a.num_pages, a.max_blocks_per_seq = 4, 3
+    a.kv_format = 0
+    a.softmax_scale = 576 ** -0.5
+    a.num_parts = 8
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_workspace_size_is_host_only(lib):
+    n = ctypes.c_size_t()
+    a = _args()
+    assert lib.mla_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    slots = 2 + 8
+    o = -(-slots * 16 * 512 * 4 // 256) * 256
+    l = -(-slots * 16 * 4 // 256) * 256
+    assert n.value == o + l
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("h_kv", 2, -2), ("d_qk", 512, -2), ("d_v", 576, -2), ("page_size", 16, -2),
+    ("kv_format", 7, -2), ("s_q", 0, -1), ("h_q", 0, -1), ("num_parts", 0, -1),
+    ("max_blocks_per_seq", 0, -1), ("topk", 5, -1), ("softmax_scale", float("inf"), -1),
+])
+def test_decode_rejects_bad_arguments_without_launching(lib, field, value, code):
+    a = _args(**{field: value})
+    assert lib.mla_decode_kvcache(ctypes.byref(a), None) == code
+    assert lib.mla_last_error() != b""
+
+
+def test_decode_rejects_null_pointers_and_small_workspace(lib):
+    a = _args()
+    assert lib.mla_decode_kvcache(ctypes.byref(a), None) == -1   # q etc. are NULL
+    fake = 0x1000   # never dereferenced: the workspace check fails first
+    a = _args(q=fake, kcache=fake, block_table=fake, cache_seqlens=fake, tile_metadata=fake,
+              num_splits=fake, out=fake, lse=fake, workspace=fake, workspace_bytes=16)
+    assert lib.mla_decode_kvcache(ctypes.byref(a), None) == -3
+    assert b"workspace" in lib.mla_last_error()
+
+
+def test_get_metadata_rejects_bad_arguments(lib):
+    assert lib.mla_get_metadata(None, None, 2, 1, 16, 2, 0, 8, None, None, None) == -2
+    assert lib.mla_get_metadata(None, None, 2, 2, 3, 1, 0, 8, None, None, None) == -1
+    assert lib.mla_get_metadata(None, None, 2, 1, 16, 1, 4, 8, None, None, None) == -1
+    assert lib.mla_get_metadata(None, None, 2, 1, 16, 1, 0, 8, None, None, None) == -1
+
+
+def test_empty_batch_decode_is_a_no_op(lib):
+    a = _args(batch=0)
+    assert lib.mla_decode_kvcache(ctypes.byref(a), None) == 0

@@ -1,0 +1,156 @@
+"""GPU parity of the HIP decode path against the fp64 oracle.
+
+Everything here goes through the Python binding into libmla's C ABI.
+Tolerances are in gpu_util.TOL.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import mla_inputs as gen
+from gpu_util import compare, log, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_paged_kv_metadata_amd as m
+    m.load_library()
+
+
+def test_tiny_workload(oracle_mod):
+    inp = gen.make_inputs(gen.CONFIGS[0], poison=True)
+    o, l, md = run_gpu(inp)
+    ro, rl = oracle_mod.decode(inp)
+    compare(o, l, ro, rl, inp.fmt, "tiny")
+
+
+def _cases():
+    rng = np.random.default_rng(2024)
+    out = []
+    for i in range(48):
+        b = int(rng.integers(1, 5))
+        s_q = int(rng.choice([1, 1, 2, 3]))
+        h_q = int(rng.choice([1, 5, 16, 16, 20, 64, 128]))
+        seqlens = [int(x) for x in rng.integers(0, 301, size=b)]
+        causal = bool(rng.integers(0, 2))
+        fmt = int(rng.integers(0, 2))
+        topk = int(rng.choice([0, 0, 0, 7, 64, 100, 130]))
+        parts = [None, 1, 8, 24][i % 4]
+        out.append((b, s_q, h_q, seqlens, causal, fmt, topk, parts, 500 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases())
+def test_random_small_shapes(oracle_mod, case):
+    b, s_q, h_q, seqlens, causal, fmt, topk, parts, seed = case
+    cfg = gen.small_config(b, s_q, h_q, seqlens, causal=causal, fmt=fmt, topk=topk, seed=seed)
+    inp = gen.make_inputs(cfg, poison=True, extra_pages=2)
+    if topk:
+        rng = np.random.default_rng(seed)
+        mask = rng.random(inp.indices.shape) < 0.2
+        inp.indices[mask] = rng.integers(-5, 400, size=int(mask.sum()))
+    log(f"case b={b} s_q={s_q} h_q={h_q} L={seqlens} causal={causal} fmt={fmt} topk={topk} parts={parts}")
+    o, l, _ = run_gpu(inp, num_parts=parts)
+    ro, rl = oracle_mod.decode(inp)
+    compare(o, l, ro, rl, fmt, "random")
+
+
+@pytest.mark.parametrize("parts", [1, 7, 8, 256, 1024])
+def test_num_parts_sweep(oracle_mod, parts):
+    cfg = gen.small_config(3, 2, 16, [700, 64, 1300], causal=True, seed=31)
+    inp = gen.make_inputs(cfg, poison=True)
+    o, l, _ = run_gpu(inp, num_parts=parts)
+    ro, rl = oracle_mod.decode(inp)
+    compare(o, l, ro, rl, inp.fmt, f"parts={parts}")
+
+
+def test_schedule_matches_oracle_bitwise():
+    from oracle import splitkv_schedule as S
+    rng = np.random.default_rng(77)
+    for trial in range(12):
+        b = int(rng.integers(1, 300))
+        sl = rng.integers(0, 20000, size=b).astype(np.int32)
+        P = int(rng.choice([1, 8, 13, 256, 1000]))
+        sparse = trial % 3 == 2
+        s_q = 2 if sparse else 1
+        import torch as T
+        slt = T.from_numpy(sl).cuda()
+        idx = None
+        if sparse:
+            topk = 300
+            ind = rng.integers(-2, 25000, size=(b, s_q, topk)).astype(np.int32)
+            idx = T.from_numpy(ind).cuda()
+            nb = S.unit_blocks_sparse(sl, ind)
+        else:
+            nb = S.unit_blocks_dense(sl)
+        from mla_paged_kv_metadata_amd import get_mla_metadata
+        md = get_mla_metadata(slt, s_q * 16, 1, s_q=s_q, indices=idx, num_parts=P)
+        T.cuda.synchronize()
+        ref_md, ref_ns = S.schedule(nb, P, 2)
+        assert np.array_equal(md.tile_metadata.cpu().numpy(), ref_md), trial
+        assert np.array_equal(md.num_splits.cpu().numpy(), ref_ns), trial
+        S.check_schedule(ref_md, ref_ns, nb)
+
+
+def test_single_key_returns_v_row_bitwise():
+    cfg = gen.small_config(3, 1, 16, [1, 1, 1], seed=41)
+    inp = gen.make_inputs(cfg, poison=True)
+    o, l, _ = run_gpu(inp)
+    for b in range(3):
+        v = gen.bf16_bits_to_f32(inp.kcache[inp.block_table[b, 0], 0, 0].view(np.uint16))[:512]
+        assert np.array_equal(o.reshape(3, 16, 512)[b], np.broadcast_to(v.astype(np.float64), (16, 512)))
+
+
+def test_zero_query_counts_keys():
+    seqlens = [1, 63, 64, 65, 127, 128, 129, 1000, 4097]
+    cfg = gen.small_config(len(seqlens), 2, 16, seqlens, causal=True, seed=42)
+    inp = gen.make_inputs(cfg, poison=True)
+    inp.q[:] = 0
+    o, l, _ = run_gpu(inp, num_parts=16)
+    l = l.reshape(len(seqlens), 2, 16)
+    for b, L in enumerate(seqlens):
+        for s in range(2):
+            n = L - 1 + s
+            if n == 0:
+                assert np.all(np.isneginf(l[b, s]))
+            else:
+                assert np.all(np.abs(l[b, s] - np.log(n)) <= 1e-5), (b, s, l[b, s, 0], np.log(n))
+
+
+def test_page_permutation_bitwise():
+    cfg = gen.small_config(3, 2, 20, [300, 65, 1000], causal=True, seed=43)
+    inp = gen.make_inputs(cfg, poison=True, extra_pages=5)
+    o1, l1, _ = run_gpu(inp)
+    o2, l2, _ = run_gpu(gen.permute_pages(inp, 5))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8])
+def test_poisoned_slots_do_not_leak(fmt):
+    cfg = gen.small_config(3, 1, 16, [37, 130, 200], fmt=fmt, seed=44)
+    clean = gen.make_inputs(cfg, poison=False, extra_pages=3)
+    dirty = gen.make_inputs(cfg, poison=True, extra_pages=3)
+    o1, l1, _ = run_gpu(clean)
+    o2, l2, _ = run_gpu(dirty)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8])
+def test_sparse_all_indices_equals_dense(oracle_mod, fmt):
+    seqlens = [300, 64, 37, 129]
+    cfg = gen.small_config(4, 1, 16, seqlens, fmt=fmt, seed=45)
+    dense = gen.make_inputs(cfg, poison=True)
+    idx = np.full((4, 1, 320), -1, dtype=np.int32)
+    for b, L in enumerate(seqlens):
+        idx[b, 0, :L] = np.arange(L)
+    sp = dataclasses.replace(dense, indices=idx)
+    od, ld, _ = run_gpu(dense)
+    osp, lsp, _ = run_gpu(sp)
+    compare(osp, lsp, od, ld, fmt, "sparse-vs-dense")

@@ -20,7 +20,7 @@ def test_hand_worked_split():
     # parts: p0 {u0b0}, p1 {u0b1,u0b2}, p2 {u0b3}, p3 {u1b0,u1b1}
     md, ns = S.schedule([4, 2], 4, 1)
     assert md[1] == 2
-    rows = md[8:].reshape(4, 8)[:, :5].tolist()
+    rows = md[8:8 + 32].reshape(4, 8)[:, :5].tolist()
     assert rows == [[0, 0, 0, 1, 0], [0, 1, 0, 3, 1], [0, 3, 0, 4, 2], [1, 0, 1, 2, 0]]
     assert list(ns) == [0, 3, 4]
 
@@ -28,10 +28,10 @@ def test_hand_worked_split():
 def test_empty_parts_and_units():
     md, ns = S.schedule([1, 1], 16, 2)
     S.check_schedule(md, ns, [1, 1])
-    rows = md[8:].reshape(16, 8)
+    rows = md[8:8 + 128].reshape(16, 8)
     assert (rows[:, 0] >= 0).sum() == 2
     md, ns = S.schedule([], 8, 2)
-    assert list(ns) == [0] and np.all(md[8::8] == -1)
+    assert list(ns) == [0] and np.all(md[8:8 + 64:8] == -1)
 
 
 @pytest.mark.parametrize("seed", range(30))
@@ -44,7 +44,7 @@ def test_random_schedules_valid_and_balanced(seed):
     md, ns = S.schedule(n, P, c0)
     S.check_schedule(md, ns, n)
     T = int(md[1])
-    rows = md[8:].reshape(P, 8)
+    rows = md[8:8 + 8 * P].reshape(P, 8)
     for p in range(P):
         u0, j0, u1, j1 = rows[p, :4]
         if u0 < 0:
