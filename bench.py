@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of MLA paged-KV decoding on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step = one pass of the whole decode path over one batch: the split-KV
+schedule (mla_get_metadata), the split-KV attention kernel and the combine
+kernel, enqueued on one stream.  The workload is the memory-bound
+variable-length decode (batch 64, 1 query token, 16 heads, lengths uniform
+in [1, 8192], bf16 pages); `value` is its KV-read bandwidth (algorithmic KV
+bytes / step time).  The compute-bound MTP decode (batch 128, 2 query
+tokens, 128 heads, L = 4096, causal) is timed the same way and reported in
+bf16 TFLOPS under "mtp"; the FP8 and sparse workloads under "fp8"/"sparse".
+
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+Three physical copies of each page pool (same logical cache, pages shuffled
+differently) are used in rotation so that consecutive steps do not hit the
+256 MB Infinity Cache.  Kernel times come from HIP events recorded on the
+launch stream around each kernel inside the timed loop.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(inp) -> dict:
+    """What the decode must move once: KV rows it attends to, q, out, lse and
+    the block-table entries it uses."""
+    import mla_inputs as gen
+    kv = inp.kv_bytes_read()
+    rows = inp.batch * inp.s_q * inp.h_q
+    n_blocks = int(sum((int(L) + 63) // 64 for L in inp.seqlens))
+    other = rows * (gen.D_QK * 2 + gen.D_V * 2 + 4) + 4 * n_blocks
+    if inp.indices is not None:
+        other += inp.indices.size * 4
+    return {"kv": kv, "total": kv + other}
+
+
+class Workload:
+    """Device-resident inputs (with pool replicas) and prepared calls."""
+
+    def __init__(self, cfg_idx: int, replicas: int):
+        import torch
+        import mla_inputs as gen
+        import mla_paged_kv_metadata_amd as m
+        self.cfg = gen.CONFIGS[cfg_idx]
+        t0 = time.time()
+        self.inp = gen.make_inputs(self.cfg)
+        log(f"[bench] {self.cfg.name}: inputs generated in {time.time() - t0:.1f}s "
+            f"({self.inp.num_pages} pages)")
+        inp = self.inp
+        dev = "cuda"
+        self.q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.seqlens = torch.from_numpy(inp.seqlens).to(dev)
+        self.indices = torch.from_numpy(inp.indices).to(dev) if inp.indices is not None else None
+        self.md = m.get_mla_metadata(self.seqlens, inp.s_q * inp.h_q, 1, s_q=inp.s_q,
+                                     indices=self.indices)
+        self.calls = []
+        out = lse = ws = None
+        for r in range(replicas):
+            v = inp if r == 0 else gen.permute_pages(inp, 7919 * r)
+            if inp.fmt == gen.FMT_BF16:
+                k = torch.from_numpy(v.kcache.view(np.int16)).view(torch.bfloat16).reshape(
+                    v.num_pages, 64, 1, 576).to(dev)
+            else:
+                k = torch.from_numpy(v.kcache).to(dev)
+            bt = torch.from_numpy(v.block_table).to(dev)
+            c = m.DecodeCall(self.q, k, bt, self.seqlens, self.md, softmax_scale=inp.softmax_scale,
+                             causal=inp.causal, indices=self.indices, out=out, lse=lse, workspace=ws)
+            out, lse, ws = c.out, c.lse, c.workspace
+            self.calls.append(c)
+        torch.cuda.synchronize()
+        self.bytes = algorithmic_bytes(inp)
+        self.flops = inp.flops()
+
+    def step(self, i, ev=None):
+        import mla_paged_kv_metadata_amd as m
+        c = self.calls[i % len(self.calls)]
+        if ev is not None:
+            ev[0].record()
+        m.refresh_mla_metadata(self.md, self.seqlens, self.indices)
+        if ev is not None:
+            ev[1].record()
+        c.partial()
+        if ev is not None:
+            ev[2].record()
+        c.combine()
+        if ev is not None:
+            ev[3].record()
+
+    def time(self, steps: int, warmup: int) -> dict:
+        import torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        md_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        part_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+        comb_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+        step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+        return {
+            "wall_ms_per_step": (t1 - t0) * 1e3 / steps,
+            "event_ms_per_step": float(step_ms.mean()),
+            "metadata_ms": float(md_ms.mean()),
+            "splitkv_ms": float(part_ms.mean()),
+            "splitkv_ms_median": float(np.median(part_ms)),
+            "combine_ms": float(comb_ms.mean()),
+        }
+
+
+def cpu_baseline(inp, target_s: float) -> dict:
+    """The fp64 oracle on a bounded sample of the same workload: whole
+    sequences (all their query rows), taken in order until about target_s of
+    CPU work; reported as KV-read GB/s over the sampled sequences."""
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    # calibrate on the first sequence
+    rows_per_b = inp.s_q * inp.h_q
+    sel0 = np.arange(rows_per_b, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.decode(inp, sel=sel0, threads=threads)
+    t_first = time.perf_counter() - t0
+    keys0 = max(int(inp.seqlens[0]), 1)
+    per_key = t_first / keys0
+    nb = 1
+    keys = keys0
+    while nb < inp.batch and (keys + int(inp.seqlens[nb])) * per_key < target_s:
+        keys += int(inp.seqlens[nb])
+        nb += 1
+    sel = np.arange(nb * rows_per_b, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.decode(inp, sel=sel, threads=threads)
+    dt = time.perf_counter() - t0
+    kv = int(sum(int(inp.seqlens[b]) for b in range(nb))) * (1152 if inp.fmt == 0 else 656)
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {nb} of {inp.batch} sequences, all {rows_per_b} query rows each "
+                      f"({kv / 1e6:.1f} MB of KV rows), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-primary", action="store_true",
+                    help="skip the MTP, FP8 and sparse workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(the decode is measured on one MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_paged_kv_metadata_amd as m
+    m.load_library()   # fails loudly without the HIP library
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    prim = Workload(1, args.replicas)
+    log("[bench] timing membound")
+    tm = prim.time(args.steps, args.warmup)
+    kv = prim.bytes["kv"]
+    value = kv / (tm["wall_ms_per_step"] * 1e-3) / 1e9
+    achieved = prim.bytes["total"] / (tm["splitkv_ms"] * 1e-3) / 1e9
+    result = {
+        "metric": "MLA paged decode: KV-read GB/s (h_q=16) and bf16 TFLOPS (h_q=128,s_q=2)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(tm["wall_ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": prim.cfg.name,
+            "batch": prim.inp.batch, "s_q": prim.inp.s_q, "h_q": prim.inp.h_q,
+            "seqlens": "uniform[1,8192], seed 1001",
+            "sum_seqlens": int(prim.inp.seqlens.sum()),
+            "kv_bytes": kv, "kv_format": "bf16", "page_size": 64,
+            "num_parts": prim.md.num_parts, "pool_replicas": args.replicas,
+        },
+        "timing_ms": {k: round(v, 5) for k, v in tm.items()},
+        "roofline": {
+            "kernel": "splitkv_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": prim.bytes["total"],
+        },
+    }
+    if not args.only_primary:
+        extra = {}
+        for idx, key in ((2, "mtp"), (3, "fp8"), (4, "sparse")):
+            del prim
+            torch.cuda.empty_cache()
+            w = Workload(idx, args.replicas)
+            log(f"[bench] timing {key}")
+            t = w.time(max(10, args.steps // 2), args.warmup)
+            step_s = t["wall_ms_per_step"] * 1e-3
+            extra[key] = {
+                "workload": w.cfg.name,
+                "ms_per_step": round(t["wall_ms_per_step"], 5),
+                "tflops": round(w.flops / step_s / 1e12, 2),
+                "kv_gbs": round(w.bytes["kv"] / step_s / 1e9, 1),
+                "splitkv_ms": round(t["splitkv_ms"], 5),
+                "combine_ms": round(t["combine_ms"], 5),
+                "metadata_ms": round(t["metadata_ms"], 5),
+                "splitkv_tflops": round(w.flops / (t["splitkv_ms"] * 1e-3) / 1e12, 2),
+                "mfma_frac_of_bf16_peak": round(w.flops / (t["splitkv_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "flops": w.flops,
+                "kv_bytes": w.bytes["kv"],
+            }
+            prim = w
+        result["secondary"] = extra
+        del prim
+    if not args.no_cpu_baseline:
+        import mla_inputs as gen
+        log("[bench] cpu baseline (oracle)")
+        inp = gen.make_inputs(gen.CONFIGS[1])
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

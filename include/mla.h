@@ -152,6 +152,20 @@ int mla_workspace_size(const mla_decode_args *args, size_t *bytes);
  */
 int mla_decode_kvcache(const mla_decode_args *args, void *stream);
 
+/*
+ * The two halves of mla_decode_kvcache, for callers that schedule them
+ * separately (e.g. to time each kernel, or to overlap the combine with
+ * other work).  mla_decode_partial enqueues only the split-KV attention
+ * kernel: sequences covered by one part get their final out/lse, split
+ * sequences leave partial results in the workspace.  mla_decode_combine
+ * enqueues only the merge of those partials (log-sum-exp weighting:
+ * lse = log sum_i exp(lse_i), out = sum_i exp(lse_i - lse) * out_i) into
+ * out/lse; it must follow mla_decode_partial on the same arguments and
+ * workspace.  Same arguments and errors as mla_decode_kvcache.
+ */
+int mla_decode_partial(const mla_decode_args *args, void *stream);
+int mla_decode_combine(const mla_decode_args *args, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *mla_last_error(void);
 

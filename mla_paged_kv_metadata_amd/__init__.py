@@ -14,5 +14,7 @@ from .api import (  # noqa: F401
     make_args,
     workspace_bytes,
     default_softmax_scale,
+    refresh_mla_metadata,
+    DecodeCall,
 )
 from ._lib import MlaError, LIB_PATH, load as load_library  # noqa: F401

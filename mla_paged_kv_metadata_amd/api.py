@@ -170,3 +170,60 @@ def mla_decode_kvcache(q: torch.Tensor, kcache: torch.Tensor, block_table: torch
 
 def default_softmax_scale() -> float:
     return 1.0 / math.sqrt(D_QK)
+
+
+def refresh_mla_metadata(metadata: MlaMetadata, cache_seqlens: torch.Tensor,
+                         indices: Optional[torch.Tensor] = None) -> MlaMetadata:
+    """Rebuild the schedule into the existing metadata buffers (no
+    allocation), e.g. at the start of every decode step."""
+    lib = _lib.load()
+    _need_i32(cache_seqlens, "cache_seqlens")
+    if cache_seqlens.shape[0] != metadata.batch:
+        raise ValueError("cache_seqlens batch differs from the metadata's")
+    dev = cache_seqlens.device
+    with torch.cuda.device(dev):
+        _lib.check(lib.mla_get_metadata(
+            ctypes.c_void_p(cache_seqlens.data_ptr()),
+            ctypes.c_void_p(indices.data_ptr() if indices is not None else None),
+            metadata.batch, metadata.s_q, metadata.q_rows_per_kv_head, 1, metadata.topk,
+            metadata.num_parts, ctypes.c_void_p(metadata.tile_metadata.data_ptr()),
+            ctypes.c_void_p(metadata.num_splits.data_ptr()), ctypes.c_void_p(_stream_ptr(dev))))
+    return metadata
+
+
+class DecodeCall:
+    """A decode call with its arguments marshalled once: run() enqueues the
+    whole decode, partial()/combine() its two kernels.  Holds references to
+    every tensor it points at."""
+
+    def __init__(self, q, kcache, block_table, cache_seqlens, metadata: MlaMetadata,
+                 softmax_scale=None, causal=False, indices=None, out=None, lse=None,
+                 workspace=None):
+        batch, s_q, h_q, _ = q.shape
+        dev = q.device
+        self.out = out if out is not None else torch.empty(batch, s_q, h_q, D_V, dtype=torch.bfloat16, device=dev)
+        self.lse = lse if lse is not None else torch.empty(batch, s_q, h_q, dtype=torch.float32, device=dev)
+        self.args = make_args(q, kcache, block_table, cache_seqlens, metadata, self.out, self.lse,
+                              softmax_scale=softmax_scale, causal=causal, indices=indices)
+        need = workspace_bytes(self.args)
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        self.args.workspace = workspace.data_ptr()
+        self.args.workspace_bytes = workspace.numel() * workspace.element_size()
+        self._keep = (q, kcache, block_table, cache_seqlens, metadata, indices)
+        self.device = dev
+        self._lib = _lib.load()
+
+    def _call(self, fn):
+        _lib.check(fn(ctypes.byref(self.args), ctypes.c_void_p(_stream_ptr(self.device))))
+
+    def run(self):
+        self._call(self._lib.mla_decode_kvcache)
+        return self.out, self.lse
+
+    def partial(self):
+        self._call(self._lib.mla_decode_partial)
+
+    def combine(self):
+        self._call(self._lib.mla_decode_combine)

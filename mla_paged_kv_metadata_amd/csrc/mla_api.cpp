@@ -188,7 +188,9 @@ MLA_EXPORT int mla_workspace_size(const mla_decode_args* args, size_t* bytes) {
   return ok();
 }
 
-MLA_EXPORT int mla_decode_kvcache(const mla_decode_args* a, void* stream) {
+namespace {
+
+int decode_impl(const mla_decode_args* a, void* stream, int which) {
   int st = check_decode_args(a);
   if (st != MLA_OK) return st;
   if (a->batch == 0) return ok();
@@ -223,7 +225,21 @@ MLA_EXPORT int mla_decode_kvcache(const mla_decode_args* a, void* stream) {
   p.row_tiles = (R + rt - 1) / rt;
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = a->softmax_scale * mla::kLog2e;
-  hipError_t e = mla::launch_decode(p, a->kv_format, (hipStream_t)stream);
+  hipError_t e = mla::launch_decode(p, a->kv_format, which, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+MLA_EXPORT int mla_decode_kvcache(const mla_decode_args* a, void* stream) {
+  return decode_impl(a, stream, 3);
+}
+
+MLA_EXPORT int mla_decode_partial(const mla_decode_args* a, void* stream) {
+  return decode_impl(a, stream, 1);
+}
+
+MLA_EXPORT int mla_decode_combine(const mla_decode_args* a, void* stream) {
+  return decode_impl(a, stream, 2);
 }

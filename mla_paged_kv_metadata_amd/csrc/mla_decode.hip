@@ -490,27 +490,32 @@ static void launch_variant(const DecodeParams& p, dim3 grid, hipStream_t stream)
     hipLaunchKernelGGL((splitkv_kernel<FMT, SPARSE, 4>), grid, dim3(kThreads), 0, stream, p);
 }
 
-hipError_t launch_decode(const DecodeParams& p, int kv_format, hipStream_t stream) {
-  const int parts8 = (p.num_parts + 7) / 8 * 8;
-  const dim3 grid(parts8 * p.row_tiles);
-  const bool sparse = p.indices != nullptr;
-  if (kv_format == 0) {
-    if (sparse)
-      launch_variant<0, true>(p, grid, stream);
-    else
-      launch_variant<0, false>(p, grid, stream);
-  } else {
-    if (sparse)
-      launch_variant<1, true>(p, grid, stream);
-    else
-      launch_variant<1, false>(p, grid, stream);
+hipError_t launch_decode(const DecodeParams& p, int kv_format, int which, hipStream_t stream) {
+  if (which & 1) {
+    const int parts8 = (p.num_parts + 7) / 8 * 8;
+    const dim3 grid(parts8 * p.row_tiles);
+    const bool sparse = p.indices != nullptr;
+    if (kv_format == 0) {
+      if (sparse)
+        launch_variant<0, true>(p, grid, stream);
+      else
+        launch_variant<0, false>(p, grid, stream);
+    } else {
+      if (sparse)
+        launch_variant<1, true>(p, grid, stream);
+      else
+        launch_variant<1, false>(p, grid, stream);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 cgrid(p.units, (p.R + 3) / 4);
-  hipLaunchKernelGGL(combine_kernel, cgrid, dim3(256), 0, stream, p.num_splits, p.ws_o, p.ws_lse,
-                     p.out, p.lse, p.R);
-  return hipGetLastError();
+  if (which & 2) {
+    const dim3 cgrid(p.units, (p.R + 3) / 4);
+    hipLaunchKernelGGL(combine_kernel, cgrid, dim3(256), 0, stream, p.num_splits, p.ws_o, p.ws_lse,
+                       p.out, p.lse, p.R);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace mla
