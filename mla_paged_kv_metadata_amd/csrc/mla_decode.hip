@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_kernel(const DecodeParams
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rb = wave % NRB;
   const int tg = wave / NRB;
   const int l16 = lane & 15;
@@ -300,7 +300,8 @@ __global__ __launch_bounds__(kThreads, 1) void splitkv_kernel(const DecodeParams
         const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
         m_run = m_new;
         l_part *= alpha;
-#pragma unroll
+        // (not force-unrolled: that makes the scheduler lift every
+        // accumulator read at once and spill other live registers)
         for (int d = 0; d < kDv / 16; ++d) o[d] *= alpha;
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 int rows_per_workgroup(int rows_per_unit) {
   if (rows_per_unit <= 16) return 16;
   if (rows_per_unit <= 32) return 32;
-  return 64;
+  return 128;   // mla_decode_wide.hip
 }
 
 template <int FMT, bool SPARSE>
@@ -484,10 +485,8 @@ static void launch_variant(const DecodeParams& p, dim3 grid, hipStream_t stream)
   const int rt = rows_per_workgroup(p.R);
   if (rt == 16)
     hipLaunchKernelGGL((splitkv_kernel<FMT, SPARSE, 1>), grid, dim3(kThreads), 0, stream, p);
-  else if (rt == 32)
-    hipLaunchKernelGGL((splitkv_kernel<FMT, SPARSE, 2>), grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((splitkv_kernel<FMT, SPARSE, 4>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((splitkv_kernel<FMT, SPARSE, 2>), grid, dim3(kThreads), 0, stream, p);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int which, hipStream_t stream) {
@@ -495,7 +494,10 @@ hipError_t launch_decode(const DecodeParams& p, int kv_format, int which, hipStr
     const int parts8 = (p.num_parts + 7) / 8 * 8;
     const dim3 grid(parts8 * p.row_tiles);
     const bool sparse = p.indices != nullptr;
-    if (kv_format == 0) {
+    if (rows_per_workgroup(p.R) == 128) {
+      hipError_t e = launch_wide(p, kv_format, grid, stream);
+      if (e != hipSuccess) return e;
+    } else if (kv_format == 0) {
       if (sparse)
         launch_variant<0, true>(p, grid, stream);
       else
