@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true",
                     help="skip the MTP, FP8 and sparse workloads")
+    ap.add_argument("--only", choices=["mtp", "fp8", "sparse"], default=None,
+                    help="time just this secondary workload (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -185,6 +187,14 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+
+    if args.only is not None:
+        idx = {"mtp": 2, "fp8": 3, "sparse": 4}[args.only]
+        w = Workload(idx, args.replicas)
+        t = w.time(args.steps, args.warmup)
+        print(json.dumps({"workload": w.cfg.name, "timing_ms": t,
+                          "splitkv_tflops": w.flops / (t["splitkv_ms"] * 1e-3) / 1e12}), flush=True)
+        return
 
     prim = Workload(1, args.replicas)
     log("[bench] timing membound")

@@ -224,6 +224,7 @@ int decode_impl(const mla_decode_args* a, void* stream, int which) {
   const int rt = mla::rows_per_workgroup(R);
   p.row_tiles = (R + rt - 1) / rt;
   p.causal = a->causal ? 1 : 0;
+  p.num_pages = a->num_pages;
   p.scale_log2 = a->softmax_scale * mla::kLog2e;
   hipError_t e = mla::launch_decode(p, a->kv_format, which, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

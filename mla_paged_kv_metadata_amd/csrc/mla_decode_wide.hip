@@ -9,27 +9,43 @@
 // with causal / sparse-index masking and bf16 or 656-byte FP8 rows.
 //
 // Design for CDNA4:
-//   * One workgroup = 8 waves = 128 query rows; wave w owns 16 rows and all
-//     64 keys of every block, so each wave's softmax is self-contained and
-//     waves only meet at the block barrier.  Two waves share a SIMD, so
-//     every MFMA keeps its accumulators in VGPRs: O^T (16 rows x 512 dims,
-//     fp32, 128 VGPRs) and the Q^T fragments (72 VGPRs) fit beside the
-//     working set.
-//   * Both products run on v_mfma_f32_16x16x32_bf16.  S^T = K Q^T with K
-//     (16 keys x 32 dims) from LDS and Q^T held in registers for the whole
-//     sequence; the 16x16 result gives each lane one query row and 4 keys,
-//     so two key tiles make exactly the 8-key B operand of O^T += V^T P^T
-//     and P never leaves registers.  V^T comes from ds_read_b64_tr_b16,
-//     which transposes 4 keys x 16 dims across a 16-lane group.
-//   * Pages are copied HBM -> LDS with global_load_lds (16 bytes per lane,
-//     no VGPR round trip), double buffered.  The 16-byte chunks of each key
-//     row are XOR-swizzled (chunk c of key t sits at c ^ swz(t) within its
-//     group of 8) so that the fragment reads spread over the LDS banks.
-//   * FP8 rows are copied raw into LDS, then dequantised (e4m3 -> fp32,
-//     times the group scale, -> bf16) into the swizzled bf16 block by all
-//     threads before the MFMA work.
+//   * One workgroup = 8 waves = 4 wave pairs x 32 query rows.  Both waves
+//     of a pair work on the same 32 rows; wave half h takes QK dims
+//     288 h .. 288 h + 287 and V dims 256 h .. 256 h + 255.  Each wave then
+//     needs only 128 VGPRs of O^T (256 dims x 32 rows, fp32) and 72 of Q^T,
+//     so two waves share a SIMD with all MFMA accumulators in VGPRs, and
+//     every MFMA is v_mfma_f32_32x32x16_bf16: a 1 KiB fragment from LDS feeds
+//     32 K flops, twice the reuse of a 16-row tile, and its 32-key read
+//     pattern hits all LDS banks once (K rows are XOR-swizzled, below).
+//   * S^T = K Q^T (32 keys x 32 rows) is contracted over each half's 288
+//     dims; the two partial tiles are exchanged through LDS and added, so
+//     both waves of a pair hold the same full S^T (the sum is commutative,
+//     hence bitwise identical) and run the same online softmax.  The 32x32
+//     result gives each lane one query row and 16 keys, which are exactly
+//     the B operand P^T of O^T += V^T P^T for two 16-key k-steps, so P never
+//     leaves registers.  V^T comes from ds_read_b64_tr_b16 (4 keys x 16 dims
+//     transposed across a 16-lane group).
+//   * Keys are staged in halves of 32 (a "slice": half of a 64-token page)
+//     through a 3-slot LDS ring filled by global_load_lds (16 bytes per
+//     lane, no VGPR round trip): two slices are in flight while the third
+//     is computed.  A bf16 slice is stored chunk-group-major: the 72 16-byte
+//     chunks of a key row form 9 groups of 8, and group G of all 32 keys is
+//     one 4 KiB block (key t at 128 t), with the chunk index XOR-swizzled
+//     within its group by a function of t, so that fragment reads of 32 keys
+//     (K) or 4 keys x 32 dims (V) spread over all LDS banks.  In this layout
+//     each lane of a copy always moves chunks of one key, so a copy address
+//     is a per-lane constant plus a scalar base.  The copies are issued from asm, so the compiler does not
+//     drain them before LDS reads; the ring waits for them itself
+//     (s_waitcnt vmcnt before a barrier).
+//   * Issuing a slice needs no vector-memory load whose wait would also
+//     drain the copies in flight: dense pages come through the scalar cache,
+//     and the pool rows of a sparse unit's index entries are resolved into
+//     an LDS table when the unit starts.
+//   * FP8 slices are copied raw into their own ring and dequantised (e4m3 ->
+//     fp32, times the group scale, -> bf16) into a bf16 slice by all threads
+//     before the MFMA work.
 //   * Key slots nobody may see are loaded from a visible key of the same
-//     block (never from outside the sequence) and their probabilities are
+//     slice (never from outside the sequence) and their probabilities are
 //     forced to zero, so V never carries stale or poisoned memory.
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -39,117 +55,189 @@ namespace wide {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 16;
-constexpr int kRowsPerWg = kRowsPerWave * kWaves;   // 128
-constexpr int kChunks = kBf16RowBytes / 16;            // 72 16-byte chunks per key row
-constexpr int kBlockBytes = kPage * kBf16RowBytes;     // 73,728
-constexpr int kRawBytes = kPage * kFp8RowBytes;        // 41,984
-constexpr int kKSteps = kDqk / 32;                     // 18
+constexpr int kRowsPerPair = 32;
+constexpr int kRowsPerWg = kRowsPerPair * (kWaves / 2);   // 128
+constexpr int kSlice = 32;                                // keys per staged slice
+constexpr int kSliceBytes = kSlice * kBf16RowBytes;       // 36,864
+constexpr int kRawSliceBytes = kSlice * kFp8RowBytes;     // 20,992
+constexpr int kKSteps = kDqk / 2 / 16;                    // 18 k-steps of 16 dims per half
+constexpr int kDimTiles = kDv / 2 / 32;                   // 8 tiles of 32 V dims per half
+constexpr int kXchgBytes = 16 * 64 * 4;                   // one wave's S^T tile, fp32
+constexpr int kGroupBytes = kSlice * 128;                 // 8 chunks of all 32 keys: 4 KiB
+constexpr int kTab = 1024;                                // sparse: resolved rows per table fill
 constexpr float kRescaleSlack = 8.f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Per-format geometry: ring slot size, copy instructions (64 lanes x 16 B)
+// per slice and per wave, and QL = k-steps of Q kept in LDS instead of
+// VGPRs (LDS: bf16 3 x 36 KiB ring + 32 KiB exchange + 16 KiB Q (+ 4 KiB
+// sparse table) = 160 KiB at most; FP8 3 x 21 KiB ring + 36 KiB slice + 32
+// + 24 (+ 4) KiB).
+template <int FMT>
+struct Geo {
+  static constexpr int kRingBytes = FMT == 0 ? kSliceBytes : (kRawSliceBytes + 1023) / 1024 * 1024;
+  static constexpr int kInst = kRingBytes / 1024;                 // 36 | 21
+  static constexpr int kPerWave = (kInst + kWaves - 1) / kWaves;  // 5 | 3
+  static constexpr int QL = FMT == 0 ? 2 : 3;
+};
+
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Bank swizzle of the 16-byte chunk index within its aligned group of 8.
-// Bits of t: s = 4*(t1^t0) + 2*t2 + (t3^t0).  Makes the 32-key x 1-chunk
-// fragment reads conflict-free and spreads the transposed 4-key reads.
+// Bank swizzle of the 16-byte chunk index within its group of 8, for key t
+// of the slice.  Bits of t: s = 4*(t1^t0) + 2*t2 + (t3^t0).
 __device__ __forceinline__ int swz(int t) {
   return ((((t >> 1) ^ t) & 1) << 2) | (((t >> 2) & 1) << 1) | (((t >> 3) ^ t) & 1);
 }
-__device__ __forceinline__ int phys_chunk(int t, int c) { return (c & ~7) | ((c ^ swz(t)) & 7); }
-
-__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// Byte offset of chunk c (dims 8 c .. 8 c + 7) of key t in a bf16 slice.
+__device__ __forceinline__ int slice_off(int t, int c) {
+  return (c >> 3) * kGroupBytes + t * 128 + 16 * ((c ^ swz(t)) & 7);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds_base + 16 l (global_load_lds_dwordx4; M0 holds the LDS base).
+// Written as asm, so the compiler neither tracks these copies nor inserts
+// waits for them.  The asm has no output registers; its address operands
+// are consumed at issue.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds_base;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are pending
+// (s_waitcnt with expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier that waits only for this wave's own LDS operations
+// (lgkmcnt), with compiler memory barriers on both sides.  (__syncthreads
+// would also drain the copies into LDS still in flight.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt: no wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // The lane id behind an empty asm: values derived from it inside a loop are
 // recomputed there (a few ALU ops) instead of being hoisted out of the loop
-// and kept live in registers, which would crowd out the Q fragments.
+// and kept live in registers.
 __device__ __forceinline__ int opaque_lane() {
   int l = threadIdx.x & 63;
   asm volatile("" : "+v"(l));
   return l;
 }
 
-// Resolve the 64 key slots of block j: lane t returns the pool row index
-// (page * 64 + slot) to load for slot t, and whether slot t is visible.
-// Masked slots get the row of a visible slot of the same block.  *mask
-// receives the wave-uniform bitmask of visible slots.
-template <bool SPARSE>
-__device__ __forceinline__ int resolve_slot(const DecodeParams& p, int b, int j, int L, int Wunit,
-                                            const int32_t* idx_row, int lane,
-                                            unsigned long long* mask) {
-  int row = 0;
-  bool ok;
-  if (!SPARSE) {
-    const int t = j * kPage + lane;
-    ok = t < L;
-    const int page = j * kPage < L ? p.block_table[(size_t)b * p.max_blocks + j] : 0;
-    const int last = min(L - 1 - j * kPage, kPage - 1);
-    row = page * kPage + (ok ? lane : max(last, 0));
-  } else {
-    const int e = j * kPage + lane;
-    const int t = e < p.topk ? idx_row[e] : -1;
-    ok = t >= 0 && t < Wunit;
-    if (ok) row = p.block_table[(size_t)b * p.max_blocks + (t >> 6)] * kPage + (t & (kPage - 1));
-    const unsigned long long m = __ballot(ok);
-    const int first = m ? __builtin_ctzll(m) : 0;
-    const int first_row = __shfl(row, first);
-    if (!ok) row = first_row;
-  }
-  *mask = __ballot(ok);
-  return row;
+// Value of lane l ^ 32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float other_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
 }
 
-// Copy block j into `dst` (bf16 rows, swizzled) or `raw` (FP8 rows, linear)
-// with global_load_lds; returns the visible-slot mask (0: nothing copied).
+// Sparse: resolve entries base .. base + count - 1 of the unit's index list
+// into tab (all threads): the pool row of the indexed key, or -1 when the
+// entry is out of range or not visible to the unit.
+__device__ __forceinline__ void fill_table(const DecodeParams& p, int32_t* tab, int b, int base, int count,
+                                           int Wunit, const int32_t* idx_row) {
+  for (int i = threadIdx.x; i < count; i += kThreads) {
+    const int e = base + i;
+    const int t = e < p.topk ? idx_row[e] : -1;
+    int v = -1;
+    if (t >= 0 && t < Wunit)
+      v = p.block_table[(size_t)b * p.max_blocks + (t >> 6)] * kPage + (t & (kPage - 1));
+    tab[i] = v;
+  }
+}
+
+// Dense: the page of block j of sequence b (0 past the end of the
+// sequence), read through the scalar cache.  Scalar loads are counted by
+// lgkmcnt, so waiting for one leaves the copies into LDS in flight.
+__device__ __forceinline__ int page_of(const DecodeParams& p, int b, int j, int L) {
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)p.block_table;
+  const int page = bt[(size_t)b * p.max_blocks + j];
+  return j * kPage < L ? page : 0;
+}
+
+// Copy slice `sl` (entries 32 sl .. 32 sl + 31 of the unit's key list) into
+// `dst` with global_load_lds.  bf16: copy instruction inst = 4 G + k of the
+// slice moves chunk group G of keys 8 k .. 8 k + 7 (lane l: key 8 k + l / 8,
+// stored chunk 8 G + l % 8, which holds logical chunk 8 G + ((l % 8) ^ swz));
+// wave w issues inst = w + 8 i, so its lanes keep one key for all i.  FP8:
+// the 656-byte rows are copied linearly (chunk q = 64 inst + lane).  Masked
+// slots load a visible row of the same slice (row 0 of the pool when the
+// slice has none).  Every wave issues exactly kPerWave loads (waves without
+// a chunk left repeat their first one), also for a slice past the unit's
+// range (active == false: row 0 of the pool, mask 0), so that every ring
+// step waits with the same vmcnt (an empty pool issues none; the waits then
+// pass at once).  Returns the mask of visible slots.
 template <int FMT, bool SPARSE>
-__device__ __forceinline__ unsigned long long issue_block(const DecodeParams& p, uint8_t* dst, int b,
-                                                          int j, int L, int Wunit,
-                                                          const int32_t* idx_row) {
+__device__ __forceinline__ uint32_t issue_slice(const DecodeParams& p, const int32_t* tab, int tab_base,
+                                                uint8_t* dst, int b, int sl, int L, bool active) {
   const int ln = opaque_lane();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  unsigned long long mask;
-  const int row = resolve_slot<SPARSE>(p, b, j, L, Wunit, idx_row, ln, &mask);
-  if (mask == 0ull) return 0ull;
-  if constexpr (FMT == 0) {
-    int dense_base = 0, dense_last = 0;
+  constexpr int kInst = Geo<FMT>::kInst;
+  constexpr int kPer = Geo<FMT>::kPerWave;
+  const int j = sl >> 1;
+  // Visible-slot mask; dense page or sparse first visible row.
+  uint32_t mask = 0u;
+  int page = 0, first_row = 0;
+  if (active) {
     if (!SPARSE) {
-      dense_base = p.block_table[(size_t)b * p.max_blocks + j] * kPage;
-      dense_last = min(L - 1 - j * kPage, kPage - 1);
+      page = page_of(p, b, j, L);
+      mask = (uint32_t)__ballot(sl * kSlice + (ln & (kSlice - 1)) < L);
+    } else {
+      const int v_own = tab[sl * kSlice + (ln & (kSlice - 1)) - tab_base];
+      mask = (uint32_t)__ballot(v_own >= 0);
+      if (mask) first_row = __builtin_amdgcn_readlane(v_own, __builtin_ctz(mask));
     }
+  }
+  if (p.num_pages == 0) return 0u;   // empty pool: no key exists, copy nothing
+  // Pool row of slot t of this slice (inactive: row 0).
+  auto row_of = [&](int t) -> int {
+    if (!active) return 0;
+    if (!SPARSE) {
+      const int tt = sl * kSlice + t;
+      return page * kPage + max(min(tt, L - 1) - j * kPage, 0);
+    }
+    const int v = tab[sl * kSlice + t - tab_base];
+    return v >= 0 ? v : first_row;
+  };
+  if constexpr (FMT == 0) {
+    const int t = 8 * (wave & 3) + (ln >> 3);
+    const uint8_t* src = p.kcache + (size_t)row_of(t) * kBf16RowBytes + 16 * ((ln & 7) ^ swz(t));
 #pragma unroll
-    for (int i = 0; i < 72 / kWaves; ++i) {
-      const int inst = wave * (72 / kWaves) + i;
-      const int q = inst * 64 + ln;
-      const int t = q / kChunks;
-      const int pc = q - t * kChunks;
-      const int c = phys_chunk(t, pc);
-      const int trow = SPARSE ? __shfl(row, t) : dense_base + min(t, dense_last);
-      lds_dma16(p.kcache + (size_t)trow * kBf16RowBytes + c * 16, dst + inst * 1024);
+    for (int i = 0; i < kPer; ++i) {
+      int inst = wave + kWaves * i;               // uniform
+      if (inst >= kInst) inst = wave;             // repeat this wave's first load
+      lds_dma16(src + 128 * (inst >> 2), dst + inst * 1024);
     }
   } else {
-    for (int inst = wave; inst < 41; inst += kWaves) {
-      const int q = inst * 64 + ln;
-      const int t = q / 41;
-      const int cc = q - t * 41;
-      const int trow = __shfl(row, t);
-      lds_dma16(p.kcache + (size_t)trow * kFp8RowBytes + cc * 16, dst + inst * 1024);
+    constexpr int kCpr = kFp8RowBytes / 16;   // 41 chunks per row
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int inst = wave + kWaves * i;
+      if (inst >= kInst) inst = wave;
+      int q = inst * 64 + ln;
+      if (q >= kSlice * kCpr) q = kSlice * kCpr - 1;   // tail: stay in the slice
+      const int t = q / kCpr;
+      const int pc = q - t * kCpr;
+      lds_dma16(p.kcache + (size_t)row_of(t) * kFp8RowBytes + pc * 16, dst + inst * 1024);
     }
   }
   return mask;
 }
 
-// Dequantise a raw FP8 block into the swizzled bf16 block (all threads).
-__device__ __forceinline__ void dequant_block(const uint8_t* raw, uint8_t* dst) {
-  for (int w = threadIdx.x; w < kPage * 40; w += kThreads) {
+// Dequantise a raw FP8 slice into the swizzled bf16 slice (all threads).
+__device__ __forceinline__ void dequant_slice(const uint8_t* raw, uint8_t* dst) {
+  // 32 keys x (32 NoPE chunks of 16 codes + 8 RoPE chunks of 8 bf16)
+  for (int w = threadIdx.x; w < kSlice * 40; w += kThreads) {
     const int t = w / 40;
     const int k = w - t * 40;
     const uint8_t* rrow = raw + t * kFp8RowBytes;
-    uint8_t* drow = dst + t * kBf16RowBytes;
     if (k < 32) {
       const u32x4 codes = *(const u32x4*)(rrow + 16 * k);
       const float s = *(const float*)(rrow + kFp8ScaleOff + 4 * (k >> 3));
@@ -161,38 +249,39 @@ __device__ __forceinline__ void dequant_block(const uint8_t* raw, uint8_t* dst) 
         wv[2 * qq] = pack_bf16x2(a[0] * s, a[1] * s);
         wv[2 * qq + 1] = pack_bf16x2(c2[0] * s, c2[1] * s);
       }
-      *(u32x4*)(drow + phys_chunk(t, 2 * k) * 16) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-      *(u32x4*)(drow + phys_chunk(t, 2 * k + 1) * 16) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+      *(u32x4*)(dst + slice_off(t, 2 * k)) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+      *(u32x4*)(dst + slice_off(t, 2 * k + 1)) = u32x4{wv[4], wv[5], wv[6], wv[7]};
     } else {
       const int rc = k - 32;
-      *(u32x4*)(drow + phys_chunk(t, 64 + rc) * 16) = *(const u32x4*)(rrow + kFp8RopeOff + 16 * rc);
+      *(u32x4*)(dst + slice_off(t, 64 + rc)) = *(const u32x4*)(rrow + kFp8RopeOff + 16 * rc);
     }
   }
 }
 
-
-template <int FMT>
-struct Smem;
-template <>
-struct Smem<0> {
-  uint8_t kb[2][kBlockBytes];     // double-buffered bf16 blocks
-  __device__ uint8_t* copy_target(int buf) { return kb[buf]; }
-};
-template <>
-struct Smem<1> {
-  uint8_t raw[2][kRawBytes];      // double-buffered FP8 rows as stored
-  uint8_t kb[1][kBlockBytes];     // the block being computed, dequantised
-  __device__ uint8_t* copy_target(int buf) { return raw[buf]; }
+template <int C>
+struct Slot {
+  static constexpr int value = C;
 };
 
 template <int FMT, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) Smem<FMT> sm;
+  using G = Geo<FMT>;
+  constexpr int QL = G::QL;
+  constexpr int QR = kKSteps - QL;   // k-steps of Q kept in registers
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[G::kRingBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[G::kRingBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[G::kRingBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbf[FMT == 1 ? kSliceBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[kWaves * kXchgBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t qs[kWaves * QL * 1024];
+  __shared__ int32_t tab[SPARSE ? kTab : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;
+  const int hf = wave & 1;    // dims half of this wave
+  const int pr = wave >> 1;   // wave pair = 32-row group
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
 
   const int bid = blockIdx.x;
   const int rest = bid >> 3;
@@ -205,8 +294,15 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
   if (u0 < 0) return;
   const int32_t* unit_blocks = p.md + kHeader + kPartRow * p.num_parts;
 
-  const int my_row = rt * kRowsPerWg + wave * kRowsPerWave + l16;
+  const int my_row = rt * kRowsPerWg + pr * kRowsPerPair + l32;
   const bool row_ok = my_row < p.R;
+  uint8_t* const qs_mine = qs + wave * QL * 1024;
+  uint8_t* const xs_mine = xs + wave * kXchgBytes;
+  const uint8_t* const xs_peer = xs + (wave ^ 1) * kXchgBytes;
+  // Logits are sc * (q . k) with sc = |scale log2 e|; a negative scale is
+  // moved into Q, so that the row max can be taken before scaling.
+  const float sc = fabsf(p.scale_log2);
+  const bool qneg = p.scale_log2 < 0.f;
 
   for (int u = u0; u <= u1; ++u) {
     const int jb = (u == u0) ? j0 : 0;
@@ -217,84 +313,157 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
     const int s_row = SPARSE ? s_unit : (row_ok ? my_row / p.h_q : 0);
     const int W = p.causal ? min(max(L - p.s_q + 1 + s_row, 0), L) : L;
     const int Wunit = (SPARSE && p.causal) ? min(max(L - p.s_q + 1 + s_unit, 0), L) : L;
+    // Dense: every row of the unit sees at least its first W_lo keys.
+    const int W_lo = p.causal ? min(max(L - p.s_q + 1, 0), L) : L;
     const int32_t* idx_row = SPARSE ? p.indices + (size_t)u * p.topk : nullptr;
+    const int s_begin = 2 * jb;   // slices of this unit's blocks
+    const int s_end = 2 * je;
+    // Sparse: the unit's index entries resolved to pool rows, kTab at a time.
+    const int pos_end = kPage * je;
+    int tab_base = kPage * jb;
+    if (SPARSE) fill_table(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
 
-    // Q^T fragments (B operand): lane holds row l16, dims 32 ks + 8 lg + 0..7.
-    bf16x8 qf[kKSteps];
+    // Q^T fragments (B operand of the 32x32x16 product): lane holds row l32,
+    // dims 288 hf + 16 ks + 8 g + 0..7.  k-steps < QR stay in registers, the
+    // rest go to this wave's LDS area.
+    bf16x8 qf[QR];
     {
-      const uint8_t* qrow = p.q + ((size_t)u * p.R + (row_ok ? my_row : 0)) * (2 * kDqk);
+      const uint8_t* qrow =
+          p.q + ((size_t)u * p.R + (row_ok ? my_row : 0)) * (2 * kDqk) + 576 * hf + 16 * g;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        u32x4 v = *(const u32x4*)(qrow + 64 * ks + 16 * lg);
+        u32x4 v = *(const u32x4*)(qrow + 32 * ks);
         if (!row_ok) v = u32x4{0, 0, 0, 0};
-        qf[ks] = __builtin_bit_cast(bf16x8, v);
+        if (qneg) v ^= 0x80008000u;   // exact bf16 negation
+        if (ks < QR)
+          qf[ks < QR ? ks : 0] = __builtin_bit_cast(bf16x8, v);
+        else
+          *(u32x4*)(qs_mine + ((ks - QR) * 64 + lane) * 16) = v;
       }
     }
+    wait_vmem<0>();
+    lds_barrier();   // tab complete
 
     float m_run = -INFINITY;
     float l_part = 0.f;
-    f32x4 o[kDv / 16];
+    f32x16 o[kDimTiles];
 #pragma unroll
-    for (int d = 0; d < kDv / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < kDimTiles; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
 
-    unsigned long long vis[2];
-    vis[0] = issue_block<FMT, SPARSE>(p, sm.copy_target(0), b, jb, L, Wunit, idx_row);
-    vis[1] = 0ull;
-    for (int j = jb; j < je; ++j) {
-      const int buf = (j - jb) & 1;
-      wait_vmem();
-      __syncthreads();   // block j is in LDS; every wave is done with block j-1
-      if (j + 1 < je)
-        vis[buf ^ 1] = issue_block<FMT, SPARSE>(p, sm.copy_target(buf ^ 1), b, j + 1, L, Wunit, idx_row);
-      const unsigned long long vmask = vis[buf];
-      if (vmask == 0ull) continue;   // no visible key in block j (uniform)
-      const uint8_t* kb;
-      if constexpr (FMT == 0) {
-        kb = sm.kb[buf];
-      } else {
-        dequant_block(sm.copy_target(buf), sm.kb[0]);
-        __syncthreads();
-        kb = sm.kb[0];
+    // Ring: slice s lives in slot (s - s_begin) % 3; two slices in flight.
+    // A unit's block range is never empty, so it has at least two slices.
+    uint32_t vis0 = issue_slice<FMT, SPARSE>(p, tab, tab_base, ring0, b, s_begin, L, true);
+    uint32_t vis1 = issue_slice<FMT, SPARSE>(p, tab, tab_base, ring1, b, s_begin + 1, L, true);
+    uint32_t vis2 = 0u;
+
+    int sl = s_begin;
+    auto step = [&](auto slot) __attribute__((always_inline)) {
+      constexpr int C = decltype(slot)::value;
+      uint8_t* const rcur = C == 0 ? ring0 : (C == 1 ? ring1 : ring2);
+      uint8_t* const rfree = C == 0 ? ring2 : (C == 1 ? ring0 : ring1);   // slot (C + 2) % 3
+      uint32_t& vcur = C == 0 ? vis0 : (C == 1 ? vis1 : vis2);
+      uint32_t& vfree = C == 0 ? vis2 : (C == 1 ? vis0 : vis1);
+      // Slice sl must be in LDS; the copy of slice sl + 1 (the last
+      // kPerWave loads of this wave) may still fly.
+      wait_vmem<G::kPerWave>();
+      lds_barrier();   // every wave is done with slice sl - 1 (slot rfree)
+      const bool more = sl + 2 < s_end;
+      if (SPARSE && more) {
+        const int pos = kSlice * (sl + 2);
+        if (pos - tab_base >= kTab) {   // the unit's range outgrew the table
+          tab_base = pos;
+          fill_table(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
+          lds_barrier();
+        }
+      }
+      vfree = issue_slice<FMT, SPARSE>(p, tab, tab_base, rfree, b, sl + 2, L, more);
+      const uint32_t vmask = vcur;
+      const int key0 = sl * kSlice;   // key index of slot 0 (dense)
+      ++sl;
+      if (vmask == 0u) return;   // no visible key in this slice (uniform)
+      const uint8_t* kb = rcur;
+      if constexpr (FMT == 1) {
+        dequant_slice(rcur, kbf);
+        lds_barrier();
+        kb = kbf;
       }
 
-      // ---- S^T = K Q^T: tile kt covers keys 16 kt + 0..15; lane holds row
-      // l16 and keys 16 kt + 4 lg + r.  The swizzle repeats every 2 k-steps
-      // (8 chunks), so two lane offsets per tile are live.
-      f32x4 sacc[4];
+      // ---- partial S^T = K Q^T over this half's 288 dims.  A = K: lane
+      // holds key l32, dims 288 hf + 16 ks + 8 g + 0..7, i.e. chunk
+      // c = 36 hf + 2 ks + g of its row, in group c / 8 = (hf ? 4 : 0) +
+      // (2 ks + 4 hf) / 8.  The swizzled position within the group repeats
+      // every 4 k-steps; four lane offsets carry it, the rest is immediate.
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
       {
         const int ln = opaque_lane();
+        const int t = ln & 31;
+        const int gg = ln >> 5;
+        const int sw = swz(t);
+        int ko[4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const int t = 16 * kt + (ln & 15);
-          const int sw = swz(t);
-          const int ko0 = t * kBf16RowBytes + (((ln >> 4) ^ sw) & 7) * 16;
-          const int ko1 = t * kBf16RowBytes + (((4 + (ln >> 4)) ^ sw) & 7) * 16;
-          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 4; ++m)
+          ko[m] = t * 128 + (((4 * hf + 2 * m + gg) ^ sw) & 7) * 16 + hf * kGroupBytes * (4 + (m >= 2 ? 1 : 0));
 #pragma unroll
-          for (int ks = 0; ks < kKSteps; ++ks) {
-            const bf16x8 a = *(const bf16x8*)(kb + ((ks & 1) ? ko1 : ko0) + (ks >> 1) * 128);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
-          }
-          sacc[kt] = acc;
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          const bf16x8 a = *(const bf16x8*)(kb + ko[ks & 3] + kGroupBytes * (ks >> 2));
+          bf16x8 bq;
+          if (ks < QR)
+            bq = qf[ks < QR ? ks : 0];
+          else
+            bq = *(const bf16x8*)(qs_mine + ((ks - QR) * 64 + ln) * 16);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, s, 0, 0, 0);
         }
+        // Keep three fragment reads ahead of the MFMA chain.
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int i = 0; i < kKSteps - 1; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      // ---- exchange the partial tiles within the pair and add.
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        *(f32x4*)(xs_mine + (qd * 64 + lane) * 16) = f32x4{s[4 * qd], s[4 * qd + 1], s[4 * qd + 2], s[4 * qd + 3]};
+      lds_barrier();
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const f32x4 v = *(const f32x4*)(xs_peer + (qd * 64 + lane) * 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[4 * qd + r] += v[r];
       }
 
-      // ---- mask + online softmax (exp2 domain).  The reference max m_run is
-      // only raised when a row's block max exceeds it by more than
-      // kRescaleSlack: P then stays below 2^kRescaleSlack and O and the row
-      // sum always share one reference.
+      // ---- mask + online softmax (exp2 domain, logit = sc * s with sc >= 0;
+      // Q carries the sign of the scale).  Lane holds row l32 and keys
+      // 8 (r >> 2) + 4 g + (r & 3) of the slice, r = 0..15.  Only a slice
+      // that some row may not see entirely is masked (uniform test).  The
+      // reference max m_run is only raised when a row's max exceeds it by
+      // more than kRescaleSlack: P then stays below 2^kRescaleSlack and O
+      // and the row sum always share one reference.
+      const bool full = SPARSE ? (vmask == 0xFFFFFFFFu) : (key0 + kSlice <= W_lo);
+      uint32_t okbits = 0xFFFFu;   // bit r: key of register r visible to this row
+      if (!full) {
+        const uint32_t lmask = vmask >> (4 * g);   // sparse: bit 8 (r >> 2) + (r & 3)
+        const int klim = W - key0 - 4 * g;         // dense: visible iff 8 (r >> 2) + (r & 3) < klim
+        okbits = 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tl = 8 * (r >> 2) + (r & 3);
+          const bool ok = SPARSE ? ((lmask >> tl) & 1u) != 0u : (tl < klim);
+          okbits |= ok ? (1u << r) : 0u;
+          s[r] = ok ? s[r] : -INFINITY;
+        }
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tl = 16 * kt + 4 * lg + r;
-          const bool ok = SPARSE ? ((vmask >> tl) & 1ull) != 0ull : (j * kPage + tl < W);
-          sacc[kt][r] = ok ? sacc[kt][r] * p.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sacc[kt][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, other_half(mx));
+      mx = mx == -INFINITY ? -INFINITY : mx * sc;
       const bool raise = mx > m_run + kRescaleSlack;
       if (__any(raise)) {
         const float m_new = raise ? mx : m_run;
@@ -302,86 +471,112 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
         m_run = m_new;
         l_part *= alpha;
 #pragma unroll
-        for (int d = 0; d < kDv / 16; ++d) o[d] *= alpha;
+        for (int d = 0; d < kDimTiles; ++d) o[d] *= alpha;
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      u32x4 pw[2];   // B operands of the two PV MFMA groups (key tiles 0+1, 2+3)
+      bf16x8 pb[2];
+      {
+        float e[16];
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        float e[8];
+        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(s[r], sc, -m_use));
+        if (!full) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[r] = fast_exp2(sacc[2 * pp][r] - m_use);
-          e[4 + r] = fast_exp2(sacc[2 * pp + 1][r] - m_use);
+          for (int r = 0; r < 16; ++r) e[r] = ((okbits >> r) & 1u) ? e[r] : 0.f;
         }
 #pragma unroll
-        for (int r = 0; r < 8; ++r) l_part += e[r];
-        pw[pp] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                       pack_bf16x2(e[6], e[7])};
+        for (int r = 0; r < 16; ++r) l_part += e[r];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          pb[kk] = __builtin_bit_cast(
+              bf16x8, u32x4{pack_bf16x2(e[8 * kk + 0], e[8 * kk + 1]), pack_bf16x2(e[8 * kk + 2], e[8 * kk + 3]),
+                            pack_bf16x2(e[8 * kk + 4], e[8 * kk + 5]), pack_bf16x2(e[8 * kk + 6], e[8 * kk + 7])});
       }
 
-      // ---- O^T += V^T P^T.  Group pp covers key tiles 2pp and 2pp+1; k-slot
-      // i of lane group lg is key 16 (2pp + (i >> 2)) + 4 lg + (i & 3).  The
-      // transposed read of 16-lane group lg takes 4 keys x 16 dims; source
-      // lane jj supplies key (jj >> 2) of the run and dims 4 (jj & 3) .. +3.
+      // ---- O^T += V^T P^T over two k-steps of 16 keys.  k-slot i of lane
+      // group g in k-step kk is key 16 kk + 8 (i >> 2) + 4 g + (i & 3) (the
+      // lane's e[8 kk + i]).  V^T rows come from two transposed reads of 4
+      // keys each: in 16-lane group G, source lane j supplies key
+      // 16 kk + 4 (G >> 1) + (j >> 2) (+ 8 for the second read) and dims
+      // 4 (j & 3) .. +3 of the group's 16-dim run 256 hf + 32 dt + 16 (G & 1).
       {
         const int ln = opaque_lane();
-        const int G = ln >> 4;
         const int jj = ln & 15;
-        const int boff = (jj & 1) * 8;              // dims 4 (jj & 3): byte 8 within a chunk
-        const int csub = (jj & 3) >> 1;             // chunk within a 16-dim tile
+        const int gb = (ln >> 4) & 1;
+        const int tA = 4 * (ln >> 5) + (jj >> 2);
+        const int tB = tA + 8;
+        const int sA = swz(tA), sB = swz(tB);
+        const int cl0 = 2 * gb + ((jj >> 1) & 1);   // chunk within its group of 8, even dt
+        const int lo = 4 * kGroupBytes * hf + 8 * (jj & 1);   // group 4 hf + dt / 2
+        const int vA0 = tA * 128 + ((cl0 ^ sA) & 7) * 16 + lo;
+        const int vA1 = tA * 128 + (((cl0 + 4) ^ sA) & 7) * 16 + lo;
+        const int vB0 = tB * 128 + ((cl0 ^ sB) & 7) * 16 + lo;
+        const int vB1 = tB * 128 + (((cl0 + 4) ^ sB) & 7) * 16 + lo;
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[pp]);
-          const int tA = 32 * pp + 4 * G + (jj >> 2);
-          const int tB = tA + 16;
-          const int sA = swz(tA), sB = swz(tB);
-          int voA[4], voB[4];
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int dq = 0; dq < 4; ++dq) {   // swizzle period: 4 dim tiles (8 chunks)
-            voA[dq] = tA * kBf16RowBytes + (((2 * dq + csub) ^ sA) & 7) * 16 + boff;
-            voB[dq] = tB * kBf16RowBytes + (((2 * dq + csub) ^ sB) & 7) * 16 + boff;
-          }
-#pragma unroll
-          for (int dt = 0; dt < kDv / 16; ++dt) {
+          for (int dt = 0; dt < kDimTiles; ++dt) {
+            const int imm = kk * 16 * 128 + kGroupBytes * (dt >> 1);
             const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(kb + voA[dt & 3] + (dt >> 2) * 128));
+                (lds_s16x4*)(kb + ((dt & 1) ? vA1 : vA0) + imm));
             const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(kb + voB[dt & 3] + (dt >> 2) * 128));
+                (lds_s16x4*)(kb + ((dt & 1) ? vB1 : vB0) + imm));
             const u32x2 xa = __builtin_bit_cast(u32x2, va);
             const u32x2 xb = __builtin_bit_cast(u32x2, vb);
             const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{xa[0], xa[1], xb[0], xb[1]});
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kk], o[dt], 0, 0, 0);
           }
+        // Keep the reads of two fragments ahead of the MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * kDimTiles - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
+    };
+    while (sl < s_end) {
+      step(Slot<0>{});
+      if (sl >= s_end) break;
+      step(Slot<1>{});
+      if (sl >= s_end) break;
+      step(Slot<2>{});
     }
 
-    // ---- epilogue: lane holds row l16, dims 16 dt + 4 lg + (0..3)
-    float l_row = l_part + __shfl_xor(l_part, 16);
-    l_row += __shfl_xor(l_row, 32);
+    // ---- epilogue: lane holds row l32, dims 256 hf + 32 dt + 8 (r >> 2) +
+    // 4 g + (r & 3).  Both halves hold the same row sum and max.
+    const float l_row = l_part + other_half(l_part);
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
     const float lse_nat =
         l_row > 0.f ? ((m_run == -INFINITY ? 0.f : m_run) + fast_log2(l_row)) * kLn2 : -INFINITY;
     const int k_u = p.num_splits[u + 1] - p.num_splits[u];
-    const int slot = p.num_splits[u] + (u == u0 ? split0 : 0);
+    const int split = p.num_splits[u] + (u == u0 ? split0 : 0);
     if (row_ok) {
       const size_t grow = (size_t)u * p.R + my_row;
+      const int dbase = 256 * hf + 4 * g;
       if (k_u == 1) {
-        uint16_t* orow = p.out + grow * kDv;
+        uint16_t* orow = p.out + grow * kDv + dbase;
 #pragma unroll
-        for (int dt = 0; dt < kDv / 16; ++dt)
-          *(u32x2*)(orow + 16 * dt + 4 * lg) = u32x2{pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
-                                                    pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
-        if (lg == 0) p.lse[grow] = lse_nat;
+        for (int dt = 0; dt < kDimTiles; ++dt)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            *(u32x2*)(orow + 32 * dt + 8 * qd) =
+                u32x2{pack_bf16x2(o[dt][4 * qd] * inv, o[dt][4 * qd + 1] * inv),
+                      pack_bf16x2(o[dt][4 * qd + 2] * inv, o[dt][4 * qd + 3] * inv)};
+        if (hf == 0 && g == 0) p.lse[grow] = lse_nat;
       } else {
-        float* orow = p.ws_o + ((size_t)slot * p.R + my_row) * kDv;
+        float* orow = p.ws_o + ((size_t)split * p.R + my_row) * kDv + dbase;
 #pragma unroll
-        for (int dt = 0; dt < kDv / 16; ++dt) *(f32x4*)(orow + 16 * dt + 4 * lg) = o[dt] * inv;
-        if (lg == 0) p.ws_lse[(size_t)slot * p.R + my_row] = lse_nat;
+        for (int dt = 0; dt < kDimTiles; ++dt)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            *(f32x4*)(orow + 32 * dt + 8 * qd) = f32x4{o[dt][4 * qd] * inv, o[dt][4 * qd + 1] * inv,
+                                                      o[dt][4 * qd + 2] * inv, o[dt][4 * qd + 3] * inv};
+        if (hf == 0 && g == 0) p.ws_lse[(size_t)split * p.R + my_row] = lse_nat;
       }
     }
-    __syncthreads();   // the next unit's first copy reuses the buffers
+    wait_vmem<0>();
+    lds_barrier();   // the next unit refills the table and the ring
   }
 }
 

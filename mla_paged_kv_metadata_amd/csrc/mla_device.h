@@ -44,8 +44,11 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return u >> 16;
 }
 
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even, in one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {

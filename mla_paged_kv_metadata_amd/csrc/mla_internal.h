@@ -24,6 +24,7 @@ struct DecodeParams {
   int R;                       // query rows per unit
   int units;
   int max_blocks, topk, num_parts, row_tiles;
+  int num_pages;               // pages in the pool (0: no key can be read)
   int causal;
   float scale_log2;            // softmax_scale * log2(e)
 };

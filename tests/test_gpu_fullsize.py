@@ -1,0 +1,44 @@
+"""GPU parity at the full benchmark workloads, in the launch configuration
+bench.py times (default number of split-KV parts), on sampled query rows
+that the oracle computes one by one."""
+import numpy as np
+import pytest
+
+import mla_inputs as gen
+from gpu_util import compare, log, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_paged_kv_metadata_amd as m
+    m.load_library()
+
+
+def _sample_rows(inp, n, seed):
+    """n rows: the first and last row, every head of the longest and the
+    shortest sequence's first query token, the rest uniform."""
+    rows = inp.batch * inp.s_q * inp.h_q
+    rng = np.random.default_rng(seed)
+    pick = {0, rows - 1}
+    for b in (int(np.argmax(inp.seqlens)), int(np.argmin(inp.seqlens))):
+        base = b * inp.s_q * inp.h_q
+        pick.update(range(base, base + min(inp.h_q, 16)))
+    pick.update(int(x) for x in rng.choice(rows, size=min(n, rows), replace=False))
+    return np.array(sorted(pick), dtype=np.int32)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_full_size_sampled_rows(oracle_mod, idx):
+    cfg = gen.CONFIGS[idx]
+    log(f"full-size {cfg.name}")
+    inp = gen.make_inputs(cfg)
+    o, l, md = run_gpu(inp)
+    sel = _sample_rows(inp, 96, 900 + idx)
+    ro, rl = oracle_mod.decode(inp, sel=sel)
+    compare(o[sel], l[sel], ro, rl, inp.fmt, f"{cfg.name} ({len(sel)} rows, {md.num_parts} parts)")

@@ -154,3 +154,42 @@ def test_sparse_all_indices_equals_dense(oracle_mod, fmt):
     od, ld, _ = run_gpu(dense)
     osp, lsp, _ = run_gpu(sp)
     compare(osp, lsp, od, ld, fmt, "sparse-vs-dense")
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_negative_scale(oracle_mod, h_q):
+    cfg = gen.small_config(2, 2, h_q, [700, 129], causal=True, seed=46)
+    inp = gen.make_inputs(cfg, poison=True)
+    inp = dataclasses.replace(inp, softmax_scale=-inp.softmax_scale)
+    o, l, _ = run_gpu(inp, num_parts=8)
+    ro, rl = oracle_mod.decode(inp)
+    compare(o, l, ro, rl, inp.fmt, f"negative scale h_q={h_q}")
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8])
+@pytest.mark.parametrize("parts", [None, 3, 40])
+def test_wide_tiles_long_sequences(oracle_mod, fmt, parts):
+    # 2 x 64 = 128 rows per sequence: the 128-row kernel, many full slices,
+    # a ragged last page, and splits that start and end inside a sequence.
+    cfg = gen.small_config(3, 2, 64, [5000, 3001, 70], causal=True, fmt=fmt, seed=47)
+    inp = gen.make_inputs(cfg, poison=True, extra_pages=2)
+    o, l, _ = run_gpu(inp, num_parts=parts)
+    ro, rl = oracle_mod.decode(inp)
+    compare(o, l, ro, rl, fmt, f"wide long fmt={fmt} parts={parts}")
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8])
+def test_sparse_topk_beyond_table(oracle_mod, fmt):
+    # topk 2500 > 1024 resolved rows per table fill: the index table of a
+    # unit is refilled while its slices stream; duplicates and invalid
+    # entries mixed in.
+    cfg = gen.small_config(2, 2, 64, [6000, 2600], causal=True, fmt=fmt, topk=2500, seed=48)
+    inp = gen.make_inputs(cfg, poison=True, extra_pages=2)
+    rng = np.random.default_rng(48)
+    mask = rng.random(inp.indices.shape) < 0.1
+    inp.indices[mask] = rng.integers(-3, 7000, size=int(mask.sum()))
+    for parts in (None, 5):
+        o, l, _ = run_gpu(inp, num_parts=parts)
+        ro, rl = oracle_mod.decode(inp)
+        compare(o, l, ro, rl, fmt, f"sparse topk=2500 fmt={fmt} parts={parts}")
+
