@@ -56,24 +56,20 @@
 //   * Key slots nobody may see are loaded from a visible key of the same
 //     slice (never from outside the sequence) and their probabilities are
 //     forced to zero, so V never carries stale or poisoned memory.
-#include "mla_device.h"
-#include "mla_internal.h"
+#include "mla_slice.h"
 
 namespace mla {
 namespace wide {
+
+using namespace slice;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerPair = 32;
 constexpr int kRowsPerWg = kRowsPerPair * (kWaves / 2);   // 128
-constexpr int kSlice = 32;                                // keys per staged slice
-constexpr int kSliceBytes = kSlice * kBf16RowBytes;       // 36,864
-constexpr int kRawSliceBytes = kSlice * kFp8RowBytes;     // 20,992
 constexpr int kKSteps = kDqk / 2 / 16;                    // 18 k-steps of 16 dims per half
 constexpr int kDimTiles = kDv / 2 / 32;                   // 8 tiles of 32 V dims per half
 constexpr int kXchgBytes = 16 * 64 * 4;                   // one wave's S^T tile, fp32
-constexpr int kGroupBytes = kSlice * 128;                 // 8 chunks of all 32 keys: 4 KiB
-constexpr int kTab = 1024;                                // sparse: resolved rows per table fill
 constexpr float kRescaleSlack = 8.f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -85,110 +81,24 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // + 24 (+ 4) KiB).
 template <int FMT>
 struct Geo {
-  static constexpr int kRingBytes = FMT == 0 ? kSliceBytes : (kRawSliceBytes + 1023) / 1024 * 1024;
+  static constexpr int kRingBytes = FMT == 0 ? kSliceBytes : kRawSlotBytes;
   static constexpr int kInst = kRingBytes / 1024;                 // 36 | 21
   static constexpr int kPerWave = (kInst + kWaves - 1) / kWaves;  // 5 | 3
   static constexpr int QL = FMT == 0 ? 2 : 3;
 };
 
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Bank swizzle of the 16-byte chunk index within its group of 8, for key t
-// of the slice.  Bits of t: s = 4*(t1^t0) + 2*t2 + (t3^t0).
-__device__ __forceinline__ int swz(int t) {
-  return ((((t >> 1) ^ t) & 1) << 2) | (((t >> 2) & 1) << 1) | (((t >> 3) ^ t) & 1);
-}
-// Byte offset of chunk c (dims 8 c .. 8 c + 7) of key t in a bf16 slice.
-__device__ __forceinline__ int slice_off(int t, int c) {
-  return (c >> 3) * kGroupBytes + t * 128 + 16 * ((c ^ swz(t)) & 7);
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes
-// land at lds_base + 16 l (global_load_lds_dwordx4; M0 holds the LDS base).
-// No instruction offset is used: it would move the LDS destination as well.
-// Written as asm, so the compiler neither tracks these copies nor inserts
-// waits for them; the callers order them against LDS reads with barriers
-// and wait for them with wait_vmem.  The asm has no output registers; its
-// address operands are consumed at issue.  It has no memory clobber, so
-// MFMAs and LDS reads of other slots may be scheduled around it; volatile
-// asm keeps its order against the barriers.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_base) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)lds_base;
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0));
-}
-
-// Wait until at most N vector-memory operations of this wave are pending
-// (s_waitcnt with expcnt and lgkmcnt left at their no-wait maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
-// Workgroup barrier that waits only for this wave's own LDS operations
-// (lgkmcnt), with compiler memory barriers on both sides.  (__syncthreads
-// would also drain the copies into LDS still in flight.)
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt: no wait
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// The lane id behind an empty asm: values derived from it inside a loop are
-// recomputed there (a few ALU ops) instead of being hoisted out of the loop
-// and kept live in registers.
-__device__ __forceinline__ int opaque_lane() {
-  int l = threadIdx.x & 63;
-  asm volatile("" : "+v"(l));
-  return l;
-}
-
-// Value of lane l ^ 32 (v_permlane32_swap: no LDS round trip).
-__device__ __forceinline__ float other_half(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
-}
-
-// Sparse: resolve entries base .. base + count - 1 of the unit's index list
-// into tab (all threads): the pool row of the indexed key, or -1 when the
-// entry is out of range or not visible to the unit.
-__device__ __forceinline__ void fill_table(const DecodeParams& p, int32_t* tab, int b, int base, int count,
-                                           int Wunit, const int32_t* idx_row) {
-  for (int i = threadIdx.x; i < count; i += kThreads) {
-    const int e = base + i;
-    const int t = e < p.topk ? idx_row[e] : -1;
-    int v = -1;
-    if (t >= 0 && t < Wunit)
-      v = p.block_table[(size_t)b * p.max_blocks + (t >> 6)] * kPage + (t & (kPage - 1));
-    tab[i] = v;
-  }
-}
-
-// Dense: the page of block j of sequence b (0 past the end of the
-// sequence), read through the scalar cache.  Scalar loads are counted by
-// lgkmcnt, so waiting for one leaves the copies into LDS in flight.
-__device__ __forceinline__ int page_of(const DecodeParams& p, int b, int j, int L) {
-  const __attribute__((address_space(4))) int32_t* bt =
-      (const __attribute__((address_space(4))) int32_t*)p.block_table;
-  const int page = bt[(size_t)b * p.max_blocks + j];
-  return j * kPage < L ? page : 0;
-}
-
 // Copy slice `sl` (entries 32 sl .. 32 sl + 31 of the unit's key list) into
-// `dst` with global_load_lds.  bf16: copy instruction inst = 4 G + k of the
-// slice moves chunk group G of keys 8 k .. 8 k + 7 (lane l: key 8 k + l / 8,
-// stored chunk 8 G + l % 8, which holds logical chunk 8 G + ((l % 8) ^ swz));
-// wave w issues inst = w + 8 i, so its lanes keep one key for all i.  FP8:
-// the 656-byte rows are copied linearly (chunk q = 64 inst + lane).  Masked
-// slots load a visible row of the same slice (row 0 of the pool when the
-// slice has none).  Every wave issues exactly kPerWave loads (waves without
-// a chunk left repeat their first one), also for a slice past the unit's
-// range (active == false: row 0 of the pool, mask 0), so that every ring
-// step waits with the same vmcnt (an empty pool issues none; the waits then
-// pass at once).  Dense slices take their page from `page` (page_of of
-// block sl / 2, loaded ahead by the caller).  Returns the mask of visible
-// slots.
+// `dst` with global_load_lds.  bf16: wave w issues copy instructions
+// inst = w + 8 i (chunk group (w >> 2) + 2 i of key octet w & 3, see
+// bf16_copy_src), so its lanes keep one key for all i.  FP8: the 656-byte
+// rows are copied linearly (chunk q = 64 inst + lane).  Masked slots load a
+// visible row of the same slice (row 0 of the pool when the slice has none).
+// Every wave issues exactly kPerWave loads (waves without a chunk left
+// repeat their first one), also for a slice past the unit's range
+// (active == false: row 0 of the pool, mask 0), so that every ring step
+// waits with the same vmcnt (an empty pool issues none; the waits then pass
+// at once).  Dense slices take their page from `page_in` (page_of of block
+// sl / 2, loaded ahead by the caller).  Returns the mask of visible slots.
 template <int FMT, bool SPARSE>
 __device__ __forceinline__ uint32_t issue_slice(const DecodeParams& p, const int32_t* tab, int tab_base,
                                                 uint8_t* dst, int sl, int L, bool active, int page_in) {
@@ -196,34 +106,13 @@ __device__ __forceinline__ uint32_t issue_slice(const DecodeParams& p, const int
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int kInst = Geo<FMT>::kInst;
   constexpr int kPer = Geo<FMT>::kPerWave;
-  const int j = sl >> 1;
-  // Visible-slot mask; dense page or sparse first visible row.
-  uint32_t mask = 0u;
-  int page = 0, first_row = 0;
-  if (active) {
-    if (!SPARSE) {
-      page = page_in;
-      mask = (uint32_t)__ballot(sl * kSlice + (ln & (kSlice - 1)) < L);
-    } else {
-      const int v_own = tab[sl * kSlice + (ln & (kSlice - 1)) - tab_base];
-      mask = (uint32_t)__ballot(v_own >= 0);
-      if (mask) first_row = __builtin_amdgcn_readlane(v_own, __builtin_ctz(mask));
-    }
-  }
+  int first_row;
+  const uint32_t mask = slice_mask<SPARSE>(tab, tab_base, sl, L, active, &first_row);
   if (p.num_pages == 0) return 0u;   // empty pool: no key exists, copy nothing
-  // Pool row of slot t of this slice (inactive: row 0).
-  auto row_of = [&](int t) -> int {
-    if (!active) return 0;
-    if (!SPARSE) {
-      const int tt = sl * kSlice + t;
-      return page * kPage + max(min(tt, L - 1) - j * kPage, 0);
-    }
-    const int v = tab[sl * kSlice + t - tab_base];
-    return v >= 0 ? v : first_row;
-  };
   if constexpr (FMT == 0) {
-    const int t = 8 * (wave & 3) + (ln >> 3);
-    const uint8_t* src = p.kcache + (size_t)row_of(t) * kBf16RowBytes + 16 * ((ln & 7) ^ swz(t));
+    const int k = wave & 3;
+    const uint8_t* src =
+        bf16_copy_src(p, slot_row<SPARSE>(tab, tab_base, sl, 8 * k + (ln >> 3), L, active, page_in, first_row), k);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       int inst = wave + kWaves * i;               // uniform
@@ -240,7 +129,8 @@ __device__ __forceinline__ uint32_t issue_slice(const DecodeParams& p, const int
       if (q >= kSlice * kCpr) q = kSlice * kCpr - 1;   // tail: stay in the slice
       const int t = q / kCpr;
       const int pc = q - t * kCpr;
-      lds_dma16(p.kcache + (size_t)row_of(t) * kFp8RowBytes + pc * 16, dst + inst * 1024);
+      const int row = slot_row<SPARSE>(tab, tab_base, sl, t, L, active, page_in, first_row);
+      lds_dma16(p.kcache + (size_t)row * kFp8RowBytes + pc * 16, dst + inst * 1024);
     }
   }
   return mask;
@@ -250,44 +140,20 @@ __device__ __forceinline__ uint32_t issue_slice(const DecodeParams& p, const int
 // rows and returns the lane's source pointer; copy_part<i>() issues part i,
 // copy instruction inst = wave + 8 i (chunk group (wave >> 2) + 2 i), if
 // inst is within the slice: waves 0-3 issue 5 parts, waves 4-7 issue 4.
-// Same rows, masks and layout as issue_slice<0, SPARSE>.
+// Same rows and layout as issue_slice<0, false>.
 struct SliceCopy {
   const uint8_t* src;   // lane's key row + its chunk within group (wave >> 2)
   uint8_t* dst;         // LDS: slot + 1 KiB x wave
   bool on;              // pool not empty
 };
-template <bool SPARSE>
-__device__ __forceinline__ SliceCopy prep_copy(const DecodeParams& p, const int32_t* tab, int tab_base,
-                                               uint8_t* slot, int sl, int L, bool active, int page_in,
-                                               uint32_t* mask_out) {
+__device__ __forceinline__ SliceCopy prep_copy(const DecodeParams& p, uint8_t* slot, int sl, int L, bool active,
+                                               int page_in) {
   const int ln = opaque_lane();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int j = sl >> 1;
-  uint32_t mask = 0u;
-  int first_row = 0;
-  if (active) {
-    if (!SPARSE) {
-      mask = (uint32_t)__ballot(sl * kSlice + (ln & (kSlice - 1)) < L);
-    } else {
-      const int v_own = tab[sl * kSlice + (ln & (kSlice - 1)) - tab_base];
-      mask = (uint32_t)__ballot(v_own >= 0);
-      if (mask) first_row = __builtin_amdgcn_readlane(v_own, __builtin_ctz(mask));
-    }
-  }
-  *mask_out = mask;
-  const int t = 8 * (wave & 3) + (ln >> 3);
-  int row = 0;
-  if (active) {
-    if (!SPARSE) {
-      const int tt = sl * kSlice + t;
-      row = page_in * kPage + max(min(tt, L - 1) - j * kPage, 0);
-    } else {
-      const int v = tab[sl * kSlice + t - tab_base];
-      row = v >= 0 ? v : first_row;
-    }
-  }
+  const int k = wave & 3;
+  const int row = slot_row<false>(nullptr, 0, sl, 8 * k + (ln >> 3), L, active, page_in, 0);
   SliceCopy c;
-  c.src = p.kcache + (size_t)row * kBf16RowBytes + 16 * ((ln & 7) ^ swz(t)) + 128 * (wave >> 2);
+  c.src = bf16_copy_src(p, row, k) + 128 * (wave >> 2);
   c.dst = slot + 1024 * wave;
   c.on = p.num_pages != 0;
   return c;
@@ -300,7 +166,6 @@ __device__ __forceinline__ void copy_part(const SliceCopy& c) {
   if (I + 1 < Geo<0>::kPerWave || wave + kWaves * I < kInst)
     lds_dma16(c.src + 256 * I, c.dst + kWaves * 1024 * I);   // group (wave >> 2) + 2 I
 }
-
 __device__ __forceinline__ void copy_all(const SliceCopy& c) {
   static_assert(Geo<0>::kPerWave == 5, "parts");
   copy_part<0>(c);
@@ -310,37 +175,6 @@ __device__ __forceinline__ void copy_all(const SliceCopy& c) {
   copy_part<4>(c);
 }
 
-// Dequantise a raw FP8 slice into the swizzled bf16 slice (all threads).
-__device__ __forceinline__ void dequant_slice(const uint8_t* raw, uint8_t* dst) {
-  // 32 keys x (32 NoPE chunks of 16 codes + 8 RoPE chunks of 8 bf16)
-  for (int w = threadIdx.x; w < kSlice * 40; w += kThreads) {
-    const int t = w / 40;
-    const int k = w - t * 40;
-    const uint8_t* rrow = raw + t * kFp8RowBytes;
-    if (k < 32) {
-      const u32x4 codes = *(const u32x4*)(rrow + 16 * k);
-      const float s = *(const float*)(rrow + kFp8ScaleOff + 4 * (k >> 3));
-      uint32_t wv[8];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[qq], false);
-        const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[qq], true);
-        wv[2 * qq] = pack_bf16x2(a[0] * s, a[1] * s);
-        wv[2 * qq + 1] = pack_bf16x2(c2[0] * s, c2[1] * s);
-      }
-      *(u32x4*)(dst + slice_off(t, 2 * k)) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-      *(u32x4*)(dst + slice_off(t, 2 * k + 1)) = u32x4{wv[4], wv[5], wv[6], wv[7]};
-    } else {
-      const int rc = k - 32;
-      *(u32x4*)(dst + slice_off(t, 64 + rc)) = *(const u32x4*)(rrow + kFp8RopeOff + 16 * rc);
-    }
-  }
-}
-
-template <int C>
-struct Slot {
-  static constexpr int value = C;
-};
 
 
 // ---- per-slice pieces shared by both kernels ------------------------------
@@ -429,7 +263,7 @@ __device__ __forceinline__ void softmax_pv(f32x16& s, f32x16 (&o)[kDimTiles], fl
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = fmaxf(mx, other_half(mx));
+  mx = fmaxf(mx, xor32(mx));
   mx = mx == -INFINITY ? -INFINITY : mx * sc;
   const bool raise = mx > m_run + kRescaleSlack;
   if (__any(raise)) {
@@ -632,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
     const int s_end = 2 * je;
     const int pos_end = kPage * je;   // sparse: index entries, resolved kTab at a time
     int tab_base = kPage * jb;
-    if (SPARSE) fill_table(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
+    if (SPARSE) fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
     bf16x8 qf[QR];
     load_q(p, u, row_base, hf, qneg, qf, qs_mine);
     wait_vmem<0>();
@@ -670,7 +504,7 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
         const int pos = kSlice * (sl + 2);
         if (pos - tab_base >= kTab) {   // the unit's range outgrew the table
           tab_base = pos;
-          fill_table(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
+          fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
           lds_barrier();
         }
       }
@@ -682,7 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
       if (vmask == 0u) return;   // no visible key in this slice (uniform)
       const uint8_t* kb = rcur;
       if constexpr (FMT == 1) {
-        dequant_slice(rcur, kbf);
+        dequant_slice<kThreads>(rcur, kbf);
         lds_barrier();
         kb = kbf;
       }
@@ -700,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
       if (sl >= s_end) break;
       step(Slot<2>{});
     }
-    store_unit(p, o, m_run, l_part + other_half(l_part), u, it.u0, it.split0, row_base, hf);
+    store_unit(p, o, m_run, l_part + xor32(l_part), u, it.u0, it.split0, row_base, hf);
     wait_vmem<0>();
     lds_barrier();   // the next unit refills the table and the ring
   }
@@ -744,7 +578,6 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
   const uint8_t* const xs_peer = xs + (wave ^ 1) * kXchgBytes;
   const float sc = fabsf(p.scale_log2);
   const bool qneg = p.scale_log2 < 0.f;
-  uint32_t unused_mask;
 
   for (int u = it.u0; u <= it.u1; ++u) {
     const int jb = (u == it.u0) ? it.j0 : 0;
@@ -769,10 +602,8 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
       for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
 
     // Slices s_begin and s_begin + 1, both groups' shares.
-    copy_all(prep_copy<false>(p, nullptr, 0, ring0, s_begin, L, true, page_of(p, b, s_begin >> 1, L),
-                              &unused_mask));
-    copy_all(prep_copy<false>(p, nullptr, 0, ring1, s_begin + 1, L, true,
-                              page_of(p, b, (s_begin + 1) >> 1, L), &unused_mask));
+    copy_all(prep_copy(p, ring0, s_begin, L, true, page_of(p, b, s_begin >> 1, L)));
+    copy_all(prep_copy(p, ring1, s_begin + 1, L, true, page_of(p, b, (s_begin + 1) >> 1, L)));
     int page_pf = page_of(p, b, min(s_begin + 2, s_end - 1) >> 1, L);
     wait_vmem<4>();               // slice s_begin (at most one slice of copies pending)
     lds_barrier();                // slice s_begin is in LDS
@@ -801,7 +632,7 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
         xchg_add(xs_peer, s, lane);
         softmax_pv<false>(s, o, m_run, l_part, rcur, vmask, key0 + kSlice <= W_lo, W, key0, sc, hf, g);
       }
-      copy_all(prep_copy<false>(p, nullptr, 0, rfree, sl + 2, L, sl + 2 < s_end, page_pf, &unused_mask));
+      copy_all(prep_copy(p, rfree, sl + 2, L, sl + 2 < s_end, page_pf));
       page_pf = page_of(p, b, min(sl + 3, s_end - 1) >> 1, L);
       if (grp == 0) wait_vmem<G::kPerWave>();   // its share of slice sl + 1
       lds_barrier();
@@ -815,7 +646,7 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
       step(Slot<2>{});
     }
     if (grp == 0) lds_barrier();   // group 0 sits out group 1's last half-step
-    store_unit(p, o, m_run, l_part + other_half(l_part), u, it.u0, it.split0, row_base, hf);
+    store_unit(p, o, m_run, l_part + xor32(l_part), u, it.u0, it.split0, row_base, hf);
     wait_vmem<0>();
     lds_barrier();   // the next unit reuses the ring
   }

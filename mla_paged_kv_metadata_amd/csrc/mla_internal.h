@@ -36,8 +36,10 @@ hipError_t launch_unit_blocks(const int32_t* seqlens, const int32_t* indices, in
                               int topk, int units, int32_t* unit_blocks, hipStream_t stream);
 hipError_t launch_schedule(int units, int num_parts, int32_t* md, int32_t* num_splits,
                            hipStream_t stream);
-// The 128-row-tile kernel (mla_decode_wide.hip).
+// The 128-row-tile kernels (mla_decode_wide.hip).
 hipError_t launch_wide(const DecodeParams& p, int kv_format, dim3 grid, hipStream_t stream);
+// The 16-row-tile kernels (mla_decode_narrow.hip).
+hipError_t launch_narrow(const DecodeParams& p, int kv_format, dim3 grid, hipStream_t stream);
 // which: 1 = split-KV attention kernel, 2 = combine kernel, 3 = both.
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int which, hipStream_t stream);
 

@@ -1,0 +1,198 @@
+// Staging of 32-key "slices" (half a 64-token page) in LDS for the gfx950
+// decode kernels: LDS layout, copies straight from global memory into LDS,
+// the waits and barriers around them, and small cross-lane helpers.
+//
+// A bf16 slice (32 keys x 576 dims) is stored chunk-group-major: the 72
+// 16-byte chunks of a key row form 9 groups of 8, and group G of all 32 keys
+// is one 4 KiB block (key t at 128 t), with the chunk index XOR-swizzled
+// within its group by a function of t.  Fragment reads of 16 or 32 keys at
+// one chunk (K operands) or of 4 keys x 32 dims (transposed V operands) then
+// hit every LDS bank once, and each lane of a copy moves chunks of a single
+// key, so a copy's address is a per-lane constant plus a scalar base.
+// An FP8 slice is copied as stored (32 rows of 656 bytes) and dequantised
+// into a bf16 slice in LDS.
+#pragma once
+
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace slice {
+
+constexpr int kSlice = 32;                              // keys per slice
+constexpr int kSliceBytes = kSlice * kBf16RowBytes;     // 36,864
+constexpr int kRawSliceBytes = kSlice * kFp8RowBytes;   // 20,992
+constexpr int kRawSlotBytes = 21 * 1024;                // FP8 slot, whole 1 KiB copies
+constexpr int kGroupBytes = kSlice * 128;               // 8 chunks of all 32 keys: 4 KiB
+constexpr int kTab = 1024;                              // sparse: resolved rows per table fill
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Bank swizzle of the 16-byte chunk index within its group of 8, for key t
+// of the slice.  Bits of t: s = 4*(t1^t0) + 2*t2 + (t3^t0).
+__device__ __forceinline__ int swz(int t) {
+  return ((((t >> 1) ^ t) & 1) << 2) | (((t >> 2) & 1) << 1) | (((t >> 3) ^ t) & 1);
+}
+// Byte offset of chunk c (dims 8 c .. 8 c + 7) of key t in a bf16 slice.
+__device__ __forceinline__ int slice_off(int t, int c) {
+  return (c >> 3) * kGroupBytes + t * 128 + 16 * ((c ^ swz(t)) & 7);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds_base + 16 l (global_load_lds_dwordx4; M0 holds the LDS base).
+// No instruction offset is used: it would move the LDS destination as well.
+// Written as asm, so the compiler neither tracks these copies nor inserts
+// waits for them; the callers order them against LDS reads with barriers
+// and wait for them with wait_vmem.  The asm has no output registers; its
+// address operands are consumed at issue.  It has no memory clobber, so
+// MFMAs and LDS reads of other buffers may be scheduled around it; volatile
+// asm keeps its order against the barriers.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds_base;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0));
+}
+
+// Wait until at most N vector-memory operations of this wave are pending
+// (s_waitcnt with expcnt and lgkmcnt left at their no-wait maxima; vmcnt is
+// split over bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that waits only for this wave's own LDS operations
+// (lgkmcnt), with compiler memory barriers on both sides.  (__syncthreads
+// would also drain the copies into LDS still in flight.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt: no wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The lane id behind an empty asm: values derived from it inside a loop are
+// recomputed there (a few ALU ops) instead of being hoisted out of the loop
+// and kept live in registers.
+__device__ __forceinline__ int opaque_lane() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
+// Value of lane l ^ 32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
+}
+// Value of lane l ^ 16 (v_permlane16_swap).
+__device__ __forceinline__ float xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return (threadIdx.x & 16) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
+}
+
+// Sparse: resolve entries base .. base + count - 1 of the unit's index list
+// into tab (all THREADS threads): the pool row of the indexed key, or -1
+// when the entry is out of range or not visible to the unit.
+template <int THREADS>
+__device__ __forceinline__ void fill_table(const DecodeParams& p, int32_t* tab, int b, int base, int count,
+                                           int Wunit, const int32_t* idx_row) {
+  for (int i = threadIdx.x; i < count; i += THREADS) {
+    const int e = base + i;
+    const int t = e < p.topk ? idx_row[e] : -1;
+    int v = -1;
+    if (t >= 0 && t < Wunit)
+      v = p.block_table[(size_t)b * p.max_blocks + (t >> 6)] * kPage + (t & (kPage - 1));
+    tab[i] = v;
+  }
+}
+
+// Dense: the page of block j of sequence b (0 past the end of the
+// sequence), read through the scalar cache.  Scalar loads are counted by
+// lgkmcnt, so waiting for one leaves the copies into LDS in flight.
+__device__ __forceinline__ int page_of(const DecodeParams& p, int b, int j, int L) {
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)p.block_table;
+  const int page = bt[(size_t)b * p.max_blocks + j];
+  return j * kPage < L ? page : 0;
+}
+
+// Pool row to load for slot t of slice sl of a unit: dense keys past the
+// sequence take its last key of the same page; sparse masked entries take
+// the slice's first visible row (first_row).  Inactive slices (past the
+// unit's range) load row 0 of the pool.
+template <bool SPARSE>
+__device__ __forceinline__ int slot_row(const int32_t* tab, int tab_base, int sl, int t, int L, bool active,
+                                        int page, int first_row) {
+  if (!active) return 0;
+  if (!SPARSE) {
+    const int j = sl >> 1;
+    const int tt = sl * kSlice + t;
+    return page * kPage + max(min(tt, L - 1) - j * kPage, 0);
+  }
+  const int v = tab[sl * kSlice + t - tab_base];
+  return v >= 0 ? v : first_row;
+}
+
+// Visible-slot mask of slice sl (bit t: slot t may be seen by some row of
+// the unit) and, for sparse units, the slice's first visible row.  Uniform.
+template <bool SPARSE>
+__device__ __forceinline__ uint32_t slice_mask(const int32_t* tab, int tab_base, int sl, int L, bool active,
+                                               int* first_row) {
+  *first_row = 0;
+  if (!active) return 0u;
+  if (!SPARSE) {
+    const int key0 = sl * kSlice;
+    return key0 >= L ? 0u : (key0 + kSlice <= L ? 0xFFFFFFFFu : (1u << (L - key0)) - 1u);
+  }
+  const int v_own = tab[sl * kSlice + (opaque_lane() & (kSlice - 1)) - tab_base];
+  const uint32_t mask = (uint32_t)__ballot(v_own >= 0);
+  if (mask) *first_row = __builtin_amdgcn_readlane(v_own, __builtin_ctz(mask));
+  return mask;
+}
+
+// Copy of a bf16 slice as 36 instructions of 64 lanes x 16 B: instruction
+// inst = 4 G + k moves chunk group G of keys 8 k .. 8 k + 7 (lane l: key
+// 8 k + l / 8, stored chunk 8 G + l % 8, which holds logical chunk
+// 8 G + ((l % 8) ^ swz)).  Lane source for key octet k:
+__device__ __forceinline__ const uint8_t* bf16_copy_src(const DecodeParams& p, int row, int k) {
+  const int ln = opaque_lane();
+  const int t = 8 * k + (ln >> 3);
+  return p.kcache + (size_t)row * kBf16RowBytes + 16 * ((ln & 7) ^ swz(t));
+}
+
+// Dequantise a raw FP8 slice into a bf16 slice (all THREADS threads).
+template <int THREADS>
+__device__ __forceinline__ void dequant_slice(const uint8_t* raw, uint8_t* dst) {
+  // 32 keys x (32 NoPE chunks of 16 codes + 8 RoPE chunks of 8 bf16)
+  for (int w = threadIdx.x; w < kSlice * 40; w += THREADS) {
+    const int t = w / 40;
+    const int k = w - t * 40;
+    const uint8_t* rrow = raw + t * kFp8RowBytes;
+    if (k < 32) {
+      const u32x4 codes = *(const u32x4*)(rrow + 16 * k);
+      const float s = *(const float*)(rrow + kFp8ScaleOff + 4 * (k >> 3));
+      uint32_t wv[8];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[qq], false);
+        const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[qq], true);
+        wv[2 * qq] = pack_bf16x2(a[0] * s, a[1] * s);
+        wv[2 * qq + 1] = pack_bf16x2(c2[0] * s, c2[1] * s);
+      }
+      *(u32x4*)(dst + slice_off(t, 2 * k)) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+      *(u32x4*)(dst + slice_off(t, 2 * k + 1)) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+    } else {
+      const int rc = k - 32;
+      *(u32x4*)(dst + slice_off(t, 64 + rc)) = *(const u32x4*)(rrow + kFp8RopeOff + 16 * rc);
+    }
+  }
+}
+
+template <int C>
+struct Slot {
+  static constexpr int value = C;
+};
+
+}  // namespace slice
+}  // namespace mla
