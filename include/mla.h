@@ -107,7 +107,7 @@ typedef struct {
 int mla_metadata_size(int batch, int s_q, int q_rows_per_kv_head, int h_kv, int topk,
                       int *num_parts, size_t *tile_metadata_elems, size_t *num_splits_elems);
 
-/* Same sizes for an explicit part count (num_parts >= 1). */
+/* Same sizes for an explicit part count (1 <= num_parts <= 2048). */
 int mla_metadata_size_for_parts(int batch, int s_q, int topk, int num_parts,
                                 size_t *tile_metadata_elems, size_t *num_splits_elems);
 
@@ -117,7 +117,7 @@ int mla_metadata_size_for_parts(int batch, int s_q, int topk, int num_parts,
  *   cache_seqlens [batch] int32 (device); indices NULL (dense) or
  *   [batch, s_q, topk] int32 (device).
  *   num_parts: normally the value mla_metadata_size returned; any value
- *   >= 1 gives a valid (if slower) schedule and must then be passed to the
+ *   in [1, 2048] gives a valid (if slower) schedule and must then be passed to the
  *   decode unchanged.
  *   tile_metadata, num_splits: device int32 arrays of the sizes above
  *   (written).  Layout of tile_metadata:

@@ -99,7 +99,8 @@ int check_decode_shape(const mla_decode_args* a) {
   if (a->topk < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "topk must be >= 0");
   if (a->topk == 0 && a->indices != nullptr)
     return fail(MLA_ERR_INVALID_ARGUMENT, "indices must be NULL when topk is 0");
-  if (a->num_parts < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts must be >= 1");
+  if (a->num_parts < 1 || a->num_parts > mla::kMaxParts)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts must be in [1, %d]", mla::kMaxParts);
   if (!std::isfinite(a->softmax_scale))
     return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
   if ((long long)a->batch * a->s_q * a->h_q > (1LL << 31) / mla::kDqk)
@@ -127,7 +128,7 @@ MLA_EXPORT const char* mla_last_error(void) { return g_last_error.c_str(); }
 
 MLA_EXPORT int mla_metadata_size_for_parts(int batch, int s_q, int topk, int num_parts,
                                            size_t* tile_metadata_elems, size_t* num_splits_elems) {
-  if (batch < 0 || s_q < 1 || topk < 0 || num_parts < 1)
+  if (batch < 0 || s_q < 1 || topk < 0 || num_parts < 1 || num_parts > mla::kMaxParts)
     return fail(MLA_ERR_INVALID_ARGUMENT, "bad batch/s_q/topk/num_parts (%d/%d/%d/%d)", batch, s_q,
                 topk, num_parts);
   if (!tile_metadata_elems || !num_splits_elems)
@@ -160,8 +161,8 @@ MLA_EXPORT int mla_get_metadata(const int32_t* cache_seqlens, const int32_t* ind
                                 int s_q, int q_rows_per_kv_head, int h_kv, int topk, int num_parts,
                                 int32_t* tile_metadata, int32_t* num_splits, void* stream) {
   if (h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv must be 1 (got %d)", h_kv);
-  if (batch < 0 || s_q < 1 || topk < 0 || num_parts < 1 || q_rows_per_kv_head < 1 ||
-      q_rows_per_kv_head % s_q != 0)
+  if (batch < 0 || s_q < 1 || topk < 0 || num_parts < 1 || num_parts > mla::kMaxParts ||
+      q_rows_per_kv_head < 1 || q_rows_per_kv_head % s_q != 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "bad batch/s_q/rows/topk/num_parts");
   if ((topk > 0) != (indices != nullptr))
     return fail(MLA_ERR_INVALID_ARGUMENT, "indices must be non-NULL exactly when topk > 0");
@@ -169,11 +170,8 @@ MLA_EXPORT int mla_get_metadata(const int32_t* cache_seqlens, const int32_t* ind
     return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
   const int units = units_of(batch, s_q, topk);
   hipStream_t s = (hipStream_t)stream;
-  int32_t* unit_blocks = tile_metadata + mla::kHeader + mla::kPartRow * num_parts;
-  hipError_t e = mla::launch_unit_blocks(cache_seqlens, indices, batch, s_q, topk, units,
-                                         unit_blocks, s);
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "unit_blocks launch: %s", hipGetErrorString(e));
-  e = mla::launch_schedule(units, num_parts, tile_metadata, num_splits, s);
+  const hipError_t e = mla::launch_metadata(cache_seqlens, indices, s_q, topk, units, num_parts,
+                                            tile_metadata, num_splits, s);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "schedule launch: %s", hipGetErrorString(e));
   return ok();
 }

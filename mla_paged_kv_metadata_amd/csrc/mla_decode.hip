@@ -21,7 +21,11 @@ namespace mla {
 // ---------------------------------------------------------------------------
 // Combine: merge the k_u partial results of every split unit.
 //   lse = log sum_i exp(lse_i);  out = sum_i exp(lse_i - lse) * O_i
-// One wave per query row; lanes own 8 output dims each.
+// One wave per query row; lanes own 8 output dims each.  The partial lses
+// are loaded by the lanes in parallel (64 at a time) and their weights are
+// formed in-lane; the partial rows are then summed four at a time, so that
+// eight 16-byte loads per lane are in flight instead of one round trip per
+// split.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ num_splits,
                                                       const float* __restrict__ ws_o,
@@ -35,8 +39,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
-  float M = -INFINITY;
-  for (int i = lane; i < k; i += 64) M = fmaxf(M, ws_lse[(size_t)(base + i) * R + r]);
+  const float* lrow = ws_lse + (size_t)base * R + r;
+  // Lane i keeps lse_i of the first 64 splits.
+  const float own = lane < k ? lrow[(size_t)lane * R] : -INFINITY;
+  float M = own;
+  for (int i = 64 + lane; i < k; i += 64) M = fmaxf(M, lrow[(size_t)i * R]);
   M = wave_max(M);
   const size_t grow = (size_t)u * R + r;
   if (M == -INFINITY) {
@@ -44,16 +51,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     if (lane == 0) lse[grow] = -INFINITY;
     return;
   }
-  float S = 0.f;
-  for (int i = lane; i < k; i += 64) S += fast_exp2((ws_lse[(size_t)(base + i) * R + r] - M) * kLog2e);
+  float S = fast_exp2((own - M) * kLog2e);
+  for (int i = 64 + lane; i < k; i += 64) S += fast_exp2((lrow[(size_t)i * R] - M) * kLog2e);
   S = wave_sum(S);
   const float lse_r = M + fast_log2(S) * kLn2;
+  const float w_own = fast_exp2((own - lse_r) * kLog2e);
+  const float* src = ws_o + ((size_t)base * R + r) * kDv + 8 * lane;
+  const size_t stride = (size_t)R * kDv;
   f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  for (int i = 0; i < k; ++i) {
-    const float w = fast_exp2((ws_lse[(size_t)(base + i) * R + r] - lse_r) * kLog2e);
-    const float* src = ws_o + ((size_t)(base + i) * R + r) * kDv + 8 * lane;
-    a0 += w * *(const f32x4*)src;
-    a1 += w * *(const f32x4*)(src + 4);
+  int i = 0;
+  for (; i + 4 <= k; i += 4) {
+    f32x4 x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = *(const f32x4*)(src + (i + j) * stride);
+      x[2 * j + 1] = *(const f32x4*)(src + (i + j) * stride + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = i + j;
+      const float w = s < 64 ? __shfl(w_own, s) : fast_exp2((lrow[(size_t)s * R] - lse_r) * kLog2e);
+      a0 += w * x[2 * j];
+      a1 += w * x[2 * j + 1];
+    }
+  }
+  for (; i < k; ++i) {
+    const float w = i < 64 ? __shfl(w_own, i) : fast_exp2((lrow[(size_t)i * R] - lse_r) * kLog2e);
+    a0 += w * *(const f32x4*)(src + i * stride);
+    a1 += w * *(const f32x4*)(src + i * stride + 4);
   }
   u32x4 wv;
   wv[0] = pack_bf16x2(a0[0], a0[1]);

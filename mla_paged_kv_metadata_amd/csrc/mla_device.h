@@ -26,6 +26,7 @@ constexpr int kHeader = 8;
 constexpr int kPartRow = 8;
 constexpr int kMagic = 0x4D4C4131;
 constexpr int kUnitOverhead = 2;  // c0: cost of one (unit, part) piece, in blocks
+constexpr int kMaxParts = 2048;   // part rows the schedule kernel assembles in LDS
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -32,9 +32,9 @@ struct DecodeParams {
 // Rows one decode workgroup covers for a given number of rows per unit.
 int rows_per_workgroup(int rows_per_unit);
 
-hipError_t launch_unit_blocks(const int32_t* seqlens, const int32_t* indices, int batch, int s_q,
-                              int topk, int units, int32_t* unit_blocks, hipStream_t stream);
-hipError_t launch_schedule(int units, int num_parts, int32_t* md, int32_t* num_splits,
+// The schedule (mla_metadata.hip); num_parts in [1, kMaxParts].
+hipError_t launch_metadata(const int32_t* seqlens, const int32_t* indices, int s_q, int topk,
+                           int units, int num_parts, int32_t* md, int32_t* num_splits,
                            hipStream_t stream);
 // The 128-row-tile kernels (mla_decode_wide.hip).
 hipError_t launch_wide(const DecodeParams& p, int kv_format, dim3 grid, hipStream_t stream);

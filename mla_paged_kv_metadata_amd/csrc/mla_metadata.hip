@@ -14,139 +14,150 @@
 // Every part thus receives at most T positions of work, and a unit is split
 // over the parts its blocks fall into.
 //
-// Two kernels: one wave per unit counts its blocks (for sparse units, up to
-// one past the last index entry that lies inside the sequence, so trailing
-// masked entries cost nothing); then a single 1024-thread workgroup scans the
-// units in chunks and writes every part's row in closed form.
+// One 1024-thread workgroup does it all in a single launch: block counts
+// (for sparse units, up to one past the last index entry that lies inside
+// the sequence, so trailing masked entries cost nothing; one wave per unit),
+// the total cost, then the units in chunks of 1024 with two workgroup scans
+// each.  The part rows are assembled in LDS and written out at the end.
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
 
-__global__ __launch_bounds__(256) void unit_blocks_kernel(const int32_t* __restrict__ seqlens,
-                                                          const int32_t* __restrict__ indices,
-                                                          int s_q, int topk, int units,
-                                                          int32_t* __restrict__ unit_blocks) {
-  const int lane = threadIdx.x & 63;
-  const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (u >= units) return;
-  int n;
-  if (indices == nullptr) {
-    const int L = seqlens[u];
-    n = (L + kPage - 1) / kPage;
-  } else {
-    const int L = seqlens[u / s_q];
-    const int32_t* idx = indices + (size_t)u * topk;
-    int last = -1;
-    for (int e = lane; e < topk; e += 64) {
-      const int t = idx[e];
-      if (t >= 0 && t < L) last = e;
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) last = max(last, __shfl_xor(last, m));
-    n = (last + 1 + kPage - 1) / kPage;
-  }
-  if (lane == 0) unit_blocks[u] = n < 1 ? 1 : n;
-}
+namespace {
 
-// Exclusive scan of one int64 value per thread over a 1024-thread block.
-// Returns the exclusive prefix; *total receives the block sum.
-__device__ long long block_exclusive_scan(long long v, long long* total, long long* sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  long long x = v;
+constexpr int kMdThreads = 1024;
+constexpr int kMdWaves = kMdThreads / 64;
+
+__device__ __forceinline__ long long wave_inclusive_scan(long long x, int lane) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const long long y = __shfl_up(x, d);
     if (lane >= d) x += y;
   }
-  if (lane == 63) sh[wave] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    long long acc = 0;
-    for (int w = 0; w < 16; ++w) {
-      const long long t = sh[w];
-      sh[w] = acc;
-      acc += t;
-    }
-    sh[16] = acc;
-  }
-  __syncthreads();
-  const long long excl = sh[wave] + x - v;
-  *total = sh[16];
-  __syncthreads();
-  return excl;
+  return x;
 }
 
-__global__ __launch_bounds__(1024) void schedule_kernel(int units, int num_parts,
-                                                        int32_t* __restrict__ md,
-                                                        int32_t* __restrict__ num_splits) {
-  __shared__ long long sh[17];
-  const int tid = threadIdx.x;
+__device__ __forceinline__ long long wave_sum(long long x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Exclusive prefix of v over the workgroup, and the workgroup total.  One
+// barrier; callers alternate between two `sh` buffers so that a buffer is
+// rewritten only after every wave has passed the next call's barrier.
+__device__ __forceinline__ long long wg_exclusive_scan(long long v, long long* sh, long long* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long incl = wave_inclusive_scan(v, lane);
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  const long long wt = wave_inclusive_scan(lane < kMdWaves ? sh[lane] : 0, lane);
+  *total = __shfl(wt, kMdWaves - 1);
+  const long long before = wave > 0 ? __shfl(wt, wave - 1) : 0;
+  return before + incl - v;
+}
+
+// Blocks of 64 keys that sparse unit u spans.  One wave.
+__device__ __forceinline__ int sparse_unit_blocks(const int32_t* __restrict__ indices, int topk, int L,
+                                                  int u, bool vec4, int lane) {
+  const int32_t* idx = indices + (size_t)u * topk;
+  int last = -1;
+  if (vec4) {
+    const int4* idx4 = (const int4*)idx;
+    for (int e4 = lane; 4 * e4 < topk; e4 += 64) {
+      const int4 t = idx4[e4];
+      if (t.x >= 0 && t.x < L) last = 4 * e4;
+      if (t.y >= 0 && t.y < L) last = 4 * e4 + 1;
+      if (t.z >= 0 && t.z < L) last = 4 * e4 + 2;
+      if (t.w >= 0 && t.w < L) last = 4 * e4 + 3;
+    }
+  } else {
+    for (int e = lane; e < topk; e += 64) {
+      const int t = idx[e];
+      if (t >= 0 && t < L) last = e;
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) last = max(last, __shfl_xor(last, m));
+  const int n = (last + 1 + kPage - 1) / kPage;
+  return n < 1 ? 1 : n;
+}
+
+__device__ __forceinline__ int dense_unit_blocks(int L) {
+  const int n = (L + kPage - 1) / kPage;
+  return n < 1 ? 1 : n;
+}
+
+}  // namespace
+
+template <bool SPARSE>
+__global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __restrict__ seqlens,
+                                                              const int32_t* __restrict__ indices,
+                                                              int s_q, int topk, int vec4, int units,
+                                                              int num_parts, int32_t* __restrict__ md,
+                                                              int32_t* __restrict__ num_splits) {
+  __shared__ long long sh[2][kMdWaves];
+  __shared__ int32_t rows[kMaxParts * kPartRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = num_parts;
   const long long c0 = kUnitOverhead;
-  const int32_t* unit_blocks = md + kHeader + kPartRow * P;
+  int32_t* unit_blocks = md + kHeader + kPartRow * P;
 
-  // Pass 1: total cost and total blocks.
-  long long cost = 0, blocks = 0;
-  for (int u = tid; u < units; u += 1024) {
-    const int nb = unit_blocks[u];
-    blocks += nb;
-    cost += nb + c0;
+  // Every part starts empty.
+  for (int i = tid; i < P * kPartRow; i += kMdThreads) {
+    const int f = i & (kPartRow - 1);
+    rows[i] = (f == 0 || f == 2) ? -1 : 0;
   }
-  long long tot_cost, tot_blocks;
-  block_exclusive_scan(cost, &tot_cost, sh);
-  block_exclusive_scan(blocks, &tot_blocks, sh);
+
+  // Block counts and the total cost.
+  long long cost = 0;
+  if (SPARSE) {
+    for (int u = wave; u < units; u += kMdWaves) {
+      const int n = sparse_unit_blocks(indices, topk, seqlens[u / s_q], u, vec4 != 0, lane);
+      if (lane == 0) {
+        unit_blocks[u] = n;
+        cost += n + c0;
+      }
+    }
+    // The counts are read back by other waves below.
+    __threadfence();
+  } else {
+    for (int u = tid; u < units; u += kMdThreads) {
+      const int n = dense_unit_blocks(seqlens[u]);
+      unit_blocks[u] = n;
+      cost += n + c0;
+    }
+  }
+  long long tot_cost;
+  wg_exclusive_scan(cost, sh[0], &tot_cost);
   const long long T = tot_cost > 0 ? (tot_cost + P - 1) / P : 1;
+  const long long tot_blocks = tot_cost - c0 * units;
 
-  if (tid == 0) {
-    md[0] = P;
-    md[1] = (int32_t)T;
-    md[2] = (int32_t)c0;
-    md[3] = units;
-    md[4] = (int32_t)tot_blocks;
-    md[5] = kMagic;
-    md[6] = 0;
-    md[7] = 0;
-    num_splits[0] = 0;
-  }
-  for (int p = tid; p < P; p += 1024) {
-    int32_t* row = md + kHeader + kPartRow * p;
-    row[0] = -1;
-    row[1] = 0;
-    row[2] = -1;
-    row[3] = 0;
-    row[4] = 0;
-    row[5] = 0;
-    row[6] = 0;
-    row[7] = 0;
-  }
-  __threadfence_block();
-  __syncthreads();
-
-  // Pass 2: unit positions, split counts and the part rows.
+  // Unit positions, split counts and the part rows, 1024 units at a time.
   long long carry_c = 0, carry_k = 0;
-  for (int base = 0; base < units; base += 1024) {
+  for (int base = 0; base < units; base += kMdThreads) {
     const int u = base + tid;
     const bool live = u < units;
-    const long long nb = live ? unit_blocks[u] : 0;
+    long long nb = 0;
+    if (live) nb = SPARSE ? unit_blocks[u] : dense_unit_blocks(seqlens[u]);
     const long long c = live ? nb + c0 : 0;
-    long long chunk_c;
-    const long long Cu = carry_c + block_exclusive_scan(c, &chunk_c, sh);
+    long long chunk_c, chunk_k;
+    const long long Cu = carry_c + wg_exclusive_scan(c, sh[1], &chunk_c);
     long long f = 0, l = -1;
     if (live) {
       f = (Cu + c0) / T;
       l = (Cu + c0 + nb - 1) / T;
     }
     const long long k = live ? l - f + 1 : 0;
-    long long chunk_k;
-    const long long Ku = carry_k + block_exclusive_scan(k, &chunk_k, sh);
+    const long long Ku = carry_k + wg_exclusive_scan(k, sh[0], &chunk_k);
     if (live) {
       num_splits[u + 1] = (int32_t)(Ku + k);
       // Parts whose first unit is u: those of u's parts that the previous
       // unit (whose last block sits at position Cu - 1) does not reach.
       const long long lo = u > 0 ? max(f, (Cu - 1) / T + 1) : f;
       for (long long p = lo; p <= l; ++p) {
-        int32_t* row = md + kHeader + kPartRow * p;
+        int32_t* row = rows + kPartRow * p;
         row[0] = u;
         row[1] = (int32_t)(p == f ? 0 : p * T - Cu - c0);
         row[4] = (int32_t)(p - f);
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int units, int num_parts
       // Parts whose last unit is u: those the next unit does not start in.
       const long long hi = (u + 1 < units) ? min(l, (Cu + c + c0) / T - 1) : l;
       for (long long p = f; p <= hi; ++p) {
-        int32_t* row = md + kHeader + kPartRow * p;
+        int32_t* row = rows + kPartRow * p;
         row[2] = u;
         row[3] = (int32_t)(p == l ? nb : (p + 1) * T - Cu - c0);
       }
@@ -162,22 +173,35 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int units, int num_parts
     carry_c += chunk_c;
     carry_k += chunk_k;
   }
+  __syncthreads();
+
+  if (tid == 0) {
+    num_splits[0] = 0;
+  }
+  if (tid < kHeader) {
+    const int32_t v = tid == 0 ? P
+                      : tid == 1 ? (int32_t)T
+                      : tid == 2 ? (int32_t)c0
+                      : tid == 3 ? units
+                      : tid == 4 ? (int32_t)tot_blocks
+                      : tid == 5 ? kMagic : 0;
+    md[tid] = v;
+  }
+  for (int i = tid; i < P * kPartRow; i += kMdThreads) md[kHeader + i] = rows[i];
 }
 
-hipError_t launch_unit_blocks(const int32_t* seqlens, const int32_t* indices, int batch, int s_q,
-                              int topk, int units, int32_t* unit_blocks, hipStream_t stream) {
-  (void)batch;
-  if (units <= 0) return hipSuccess;
-  const int grid = (units + 3) / 4;
-  hipLaunchKernelGGL(unit_blocks_kernel, dim3(grid), dim3(256), 0, stream, seqlens, indices, s_q,
-                     topk, units, unit_blocks);
-  return hipGetLastError();
-}
-
-hipError_t launch_schedule(int units, int num_parts, int32_t* md, int32_t* num_splits,
+hipError_t launch_metadata(const int32_t* seqlens, const int32_t* indices, int s_q, int topk,
+                           int units, int num_parts, int32_t* md, int32_t* num_splits,
                            hipStream_t stream) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(1024), 0, stream, units, num_parts, md,
-                     num_splits);
+  if (num_parts < 1 || num_parts > kMaxParts) return hipErrorInvalidValue;
+  if (indices == nullptr) {
+    hipLaunchKernelGGL(metadata_kernel<false>, dim3(1), dim3(kMdThreads), 0, stream, seqlens, indices,
+                       s_q, topk, 0, units, num_parts, md, num_splits);
+  } else {
+    const int vec4 = (topk % 4 == 0) && ((uintptr_t)indices % 16 == 0);
+    hipLaunchKernelGGL(metadata_kernel<true>, dim3(1), dim3(kMdThreads), 0, stream, seqlens, indices,
+                       s_q, topk, vec4, units, num_parts, md, num_splits);
+  }
   return hipGetLastError();
 }
 

@@ -57,6 +57,8 @@ def test_metadata_size_for_parts(lib):
     assert lib.mla_metadata_size_for_parts(-1, 1, 0, 8, ctypes.byref(md), ctypes.byref(ns)) == -1
     assert lib.mla_metadata_size_for_parts(1, 1, 0, 0, ctypes.byref(md), ctypes.byref(ns)) == -1
     assert b"num_parts" in lib.mla_last_error()
+    assert lib.mla_metadata_size_for_parts(1, 1, 0, 2048, ctypes.byref(md), ctypes.byref(ns)) == 0
+    assert lib.mla_metadata_size_for_parts(1, 1, 0, 2049, ctypes.byref(md), ctypes.byref(ns)) == -1
 
 
 def _args(**kw):
@@ -85,7 +87,7 @@ def test_workspace_size_is_host_only(lib):
 
 @pytest.mark.parametrize("field,value,code", [
     ("h_kv", 2, -2), ("d_qk", 512, -2), ("d_v", 576, -2), ("page_size", 16, -2),
-    ("kv_format", 7, -2), ("s_q", 0, -1), ("h_q", 0, -1), ("num_parts", 0, -1),
+    ("kv_format", 7, -2), ("s_q", 0, -1), ("h_q", 0, -1), ("num_parts", 0, -1), ("num_parts", 2049, -1),
     ("max_blocks_per_seq", 0, -1), ("topk", 5, -1), ("softmax_scale", float("inf"), -1),
 ])
 def test_decode_rejects_bad_arguments_without_launching(lib, field, value, code):

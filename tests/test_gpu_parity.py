@@ -74,17 +74,19 @@ def test_num_parts_sweep(oracle_mod, parts):
 def test_schedule_matches_oracle_bitwise():
     from oracle import splitkv_schedule as S
     rng = np.random.default_rng(77)
-    for trial in range(12):
-        b = int(rng.integers(1, 300))
+    for trial in range(16):
+        # trials 12..15: more than 1024 units (several scan chunks), the
+        # largest part count, and index rows that are not 16-byte multiples
+        b = int(rng.integers(1, 300)) if trial < 12 else int(rng.integers(1025, 2600))
         sl = rng.integers(0, 20000, size=b).astype(np.int32)
-        P = int(rng.choice([1, 8, 13, 256, 1000]))
+        P = int(rng.choice([1, 8, 13, 256, 1000])) if trial < 12 else int(rng.choice([7, 2048]))
         sparse = trial % 3 == 2
         s_q = 2 if sparse else 1
         import torch as T
         slt = T.from_numpy(sl).cuda()
         idx = None
         if sparse:
-            topk = 300
+            topk = 300 if trial < 12 else 61
             ind = rng.integers(-2, 25000, size=(b, s_q, topk)).astype(np.int32)
             idx = T.from_numpy(ind).cuda()
             nb = S.unit_blocks_sparse(sl, ind)
