@@ -123,7 +123,8 @@ int mla_metadata_size_for_parts(int batch, int s_q, int topk, int num_parts,
  *   (written).  Layout of tile_metadata:
  *     [0..7]   header {num_parts, T, c0, units, total_blocks, 0x4D4C4131, 0, 0}
  *     [8 + 8p .. 8 + 8p + 7] part p: {u_first, j_first, u_last, j_end,
- *              split index of u_first, 0, 0, 0}; an empty part has u_first -1
+ *              split index of u_first, cache_seqlens of u_first's sequence,
+ *              blocks of u_first, 0}; an empty part has u_first -1
  *     [8 + 8P + u] blocks of 64 keys that unit u spans
  *   where a unit is a sequence (dense) or a (sequence, query token) pair
  *   (sparse).  num_splits[u+1] - num_splits[u] is the number of parts unit u

@@ -8,30 +8,29 @@
 // sequence (V = first 512 dims), out + natural-log lse, with causal /
 // sparse-index masking and bf16 or 656-byte FP8 rows.
 //
-// Design for CDNA4, where these shapes only have to stream the cache:
-//   * One workgroup = 4 waves = 16 query rows.  Keys stream through an LDS
-//     ring of 32-key slices filled by global_load_lds (no VGPR round trip);
-//     with bf16 pages the ring has 4 slots, three slices (108 KiB) in flight
-//     while the fourth is computed, enough to cover the HBM latency at full
-//     bandwidth with one workgroup per CU (3 slots when a sparse index table
-//     also needs LDS).
-//   * The 16 rows x 32 keys of a slice are split over the waves by the
-//     contraction dims: wave w computes the partial S^T over its share of
-//     the 18 QK k-steps (32 dims each; 5, 5, 4, 4) with
-//     v_mfma_f32_16x16x32_bf16, the four partial tiles are summed through
-//     LDS in a fixed order (so every wave holds the same S^T), every wave
-//     runs the same online softmax, and wave w accumulates O^T for V dims
-//     128 w .. 128 w + 127.  One barrier per slice serves the exchange, the
-//     arrival of the next slice and the release of the oldest slot; the
-//     exchange buffer alternates between two halves by slice parity, so a
-//     wave that runs ahead never overwrites tiles still being read.
-//   * The 16x16 S^T tiles give each lane one row and 8 keys, which are the
-//     B operand P^T of the 16x16x32 PV product (the k order of V^T follows
-//     them), so P never leaves registers; V^T comes from ds_read_b64_tr_b16.
-//   * FP8 slices are copied raw and dequantised into one bf16 slice by all
-//     threads before their QK (two more barriers per slice).
+// Design for CDNA4, where these shapes only have to stream the cache and
+// the one wave per SIMD that the LDS ring leaves room for has no other wave
+// to hide its latencies behind, so every step is built to be short:
+//   * One workgroup = 4 waves = 16 query rows, one step = one 64-token page.
+//     Pages stream through two LDS page slots filled by global_load_lds (no
+//     VGPR round trip): page p + 1 is in flight while page p is computed.
+//   * QK: wave w computes the full S^T tile of keys 16 w .. 16 w + 15 over
+//     all 576 dims (18 v_mfma_f32_16x16x32_bf16, Q^T kept in registers for
+//     the whole unit), so there are no partial sums to reduce; the four 1 KiB
+//     tiles are exchanged through LDS once per page, after which every wave
+//     holds the whole 16 x 64 S^T and runs the same online softmax.
+//   * The 16x16 S^T tiles give each lane one row and 16 keys, which are the
+//     B operand P^T of the 16x16x32 PV products (the k order of V^T follows
+//     them), so P never leaves registers; wave w accumulates O^T for V dims
+//     128 w .. 128 w + 127 from ds_read_b64_tr_b16 reads of V^T.
+//   * Two barriers per page: one for the page's arrival (which also frees
+//     the other slot for the next page), one for the S^T exchange.
+//   * FP8 pages are copied raw and dequantised into one bf16 page by all
+//     threads after the arrival barrier (one more barrier per page).
+//   * Page numbers of a dense unit are held one per lane and read with
+//     v_readlane, so issuing a copy needs no memory access of its own.
 //   * Key slots nobody may see are loaded from a visible key of the same
-//     slice and their probabilities forced to zero.
+//     half page and their probabilities forced to zero.
 #include "mla_slice.h"
 
 namespace mla {
@@ -42,54 +41,60 @@ using namespace slice;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 16;
-constexpr int kQKSteps = 5;                   // QK k-steps per wave (the last two waves: 4 + a zero step)
+constexpr int kKSteps = kDqk / 32;            // 18 QK k-steps of 32 dims
 constexpr int kDimTiles = kDv / 16 / kWaves;  // 8 tiles of 16 V dims per wave
-constexpr int kXchgBytes = 8 * 64 * 4;        // one wave's partial S^T: 2 tiles x 4 fp32 per lane
+constexpr int kPageBf16 = 2 * kSliceBytes;    // 73,728
+constexpr int kRawPage = kPage * kFp8RowBytes;  // 41,984 = 41 x 1 KiB
+constexpr int kRawInst = kRawPage / 1024;       // 41
+constexpr int kXchgBytes = kWaves * 1024;       // four 16 x 16 fp32 tiles
 constexpr float kRescaleSlack = 8.f;
 
-// LDS: bf16 dense 4 x 36 KiB + 2 x 8 KiB exchange = 160 KiB; bf16 sparse
-// 3 slots + 16 KiB + 4 KiB table; FP8 4 x 21 KiB raw + 36 KiB dequantised
-// slice + 16 + 4 KiB.
-template <int FMT>
+// LDS: bf16 2 x 72 KiB + 4 KiB exchange (+ 4 KiB sparse table); FP8 2 x 41 KiB
+// raw + 72 KiB dequantised page + 4 KiB (+ 2 KiB table): at most 160 KiB.
+template <int FMT, bool SPARSE>
 struct Geo {
-  static constexpr int kRingBytes = FMT == 0 ? kSliceBytes : kRawSlotBytes;
-  static constexpr int kInst = kRingBytes / 1024;                 // 36 | 21
-  static constexpr int kPerWave = kInst / kWaves;                 // 9 | 5 (wave 0 of FP8: 6)
-  static constexpr int kMaxPerWave = (kInst + kWaves - 1) / kWaves;
+  static constexpr int kSlotBytes = FMT == 0 ? kPageBf16 : kRawPage;
+  static constexpr int kTabN = (FMT == 1 && SPARSE) ? 512 : kTab;
 };
 
-// First QK k-step of wave w (18 = 5 + 5 + 4 + 4); ks_begin(4) = 18.
-__device__ __forceinline__ int ks_begin(int w) { return w <= 2 ? 5 * w : (w == 3 ? 14 : 18); }
-
-// Copy slice sl of the unit into slot dst (this wave's share).  bf16: wave
-// w issues instructions w + 4 i, i.e. key octet w, chunk group i.  FP8:
-// rows copied linearly, chunk q = 64 inst + lane.  Returns the slice's
-// visible-slot mask (uniform).
+// Copy page j of the unit's key list into an LDS slot (this wave's share)
+// and return its visible-key mask (bit 32 h + t: key t of half h).  bf16:
+// per half, wave w issues instructions w + 4 i (key octet w, chunk group i).
+// FP8: the 64 raw rows are copied linearly, 16-byte chunk q = 64 inst + lane.
 template <int FMT, bool SPARSE>
-__device__ __forceinline__ uint32_t copy_slice(const DecodeParams& p, const int32_t* tab, int tab_base,
-                                               uint8_t* dst, int sl, int L, bool active, int page) {
-  const int ln = opaque_lane();
+__device__ __forceinline__ uint64_t copy_page(const DecodeParams& p, const int32_t* tab, int tab_base, uint8_t* dst,
+                                              int j, int L, int page) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int first_row;
-  const uint32_t mask = slice_mask<SPARSE>(tab, tab_base, sl, L, active, &first_row);
+  int fr0, fr1;
+  const uint32_t m0 = slice_mask<SPARSE>(tab, tab_base, 2 * j, L, true, &fr0);
+  const uint32_t m1 = slice_mask<SPARSE>(tab, tab_base, 2 * j + 1, L, true, &fr1);
+  const uint64_t mask = (uint64_t)m0 | ((uint64_t)m1 << 32);
+  // A half without a visible key still goes through PV (with zero
+  // probabilities): it loads the other half's first visible row.
+  if (m0 == 0u) fr0 = fr1;
+  if (m1 == 0u) fr1 = fr0;
   if (p.num_pages == 0) return 0u;   // empty pool: no key exists, copy nothing
   if constexpr (FMT == 0) {
-    const uint8_t* src =
-        bf16_copy_src(p, slot_row<SPARSE>(tab, tab_base, sl, 8 * wave + (ln >> 3), L, active, page, first_row),
-                      wave);
+    const int ln = opaque_lane();
+    const int t = 8 * wave + (ln >> 3);
+    const uint8_t* s0 = bf16_copy_src(p, slot_row<SPARSE>(tab, tab_base, 2 * j, t, L, true, page, fr0), wave);
+    const uint8_t* s1 = bf16_copy_src(p, slot_row<SPARSE>(tab, tab_base, 2 * j + 1, t, L, true, page, fr1), wave);
 #pragma unroll
-    for (int i = 0; i < Geo<0>::kPerWave; ++i) lds_dma16(src + 128 * i, dst + 1024 * (wave + kWaves * i));
+    for (int i = 0; i < 9; ++i) lds_dma16(s0 + 128 * i, dst + 1024 * (wave + kWaves * i));
+#pragma unroll
+    for (int i = 0; i < 9; ++i) lds_dma16(s1 + 128 * i, dst + kSliceBytes + 1024 * (wave + kWaves * i));
   } else {
     constexpr int kCpr = kFp8RowBytes / 16;   // 41 chunks per row
+    const int ln = opaque_lane();
 #pragma unroll
-    for (int i = 0; i < Geo<1>::kMaxPerWave; ++i) {
+    for (int i = 0; i < (kRawInst + kWaves - 1) / kWaves; ++i) {
       const int inst = wave + kWaves * i;
-      if (inst < Geo<1>::kInst) {
-        int q = inst * 64 + ln;
-        if (q >= kSlice * kCpr) q = kSlice * kCpr - 1;   // tail: stay in the slice
-        const int t = q / kCpr;
+      if (inst < kRawInst) {
+        const int q = inst * 64 + ln;
+        const int t = q / kCpr;   // row of the page, 0..63
         const int pc = q - t * kCpr;
-        const int row = slot_row<SPARSE>(tab, tab_base, sl, t, L, active, page, first_row);
+        const int h = t >> 5;
+        const int row = slot_row<SPARSE>(tab, tab_base, 2 * j + h, t & 31, L, true, page, h ? fr1 : fr0);
         lds_dma16(p.kcache + (size_t)row * kFp8RowBytes + pc * 16, dst + inst * 1024);
       }
     }
@@ -99,15 +104,12 @@ __device__ __forceinline__ uint32_t copy_slice(const DecodeParams& p, const int3
 
 template <int FMT, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams p) {
-  using G = Geo<FMT>;
-  constexpr int NS = (FMT == 0 && SPARSE) ? 3 : 4;   // ring slots
-  __shared__ __attribute__((aligned(1024))) uint8_t ring0[G::kRingBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring1[G::kRingBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[G::kRingBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring3[NS == 4 ? G::kRingBytes : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t kbf[FMT == 1 ? kSliceBytes : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t xs[2 * kWaves * kXchgBytes];
-  __shared__ int32_t tab[SPARSE ? kTab : 1];
+  using G = Geo<FMT, SPARSE>;
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[G::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[G::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbf[FMT == 1 ? kPageBf16 : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[kXchgBytes];
+  __shared__ int32_t tab[SPARSE ? G::kTabN : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -120,10 +122,11 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
   const int rt = rest % p.row_tiles;
   const int part = (rest / p.row_tiles) * 8 + (bid & 7);
   if (part >= p.num_parts) return;
-  if (p.md[0] != p.num_parts || p.md[5] != kMagic || p.md[3] != p.units) return;
+  // Header and part row are read together (one round trip).
   const int32_t* prow = p.md + kHeader + kPartRow * part;
+  const int h0 = p.md[0], h3 = p.md[3], h5 = p.md[5];
   const int u0 = prow[0], j0 = prow[1], u1 = prow[2], j1 = prow[3], split0 = prow[4];
-  if (u0 < 0) return;
+  if (h0 != p.num_parts || h5 != kMagic || h3 != p.units || u0 < 0) return;
   const int32_t* unit_blocks = p.md + kHeader + kPartRow * p.num_parts;
 
   const int row_base = rt * kRows;   // uniform
@@ -131,43 +134,68 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
   const bool row_ok = my_row < p.R;
   const float sc = fabsf(p.scale_log2);
   const bool qneg = p.scale_log2 < 0.f;   // the sign goes into Q
-  const int ks0 = ks_begin(wave);
-  const int nks = ks_begin(wave + 1) - ks0;   // 5 or 4
 
+  // Length and block count of the current unit: the part row carries them
+  // for the first unit; those of the next are prefetched at each unit start.
+  int L_nx = prow[5], n_nx = prow[6];
   for (int u = u0; u <= u1; ++u) {
     const int jb = (u == u0) ? j0 : 0;
-    const int je = (u == u1) ? j1 : unit_blocks[u];
+    const int je = (u == u1) ? j1 : n_nx;
     const int b = SPARSE ? u / p.s_q : u;
-    const int L = p.seqlens[b];
+    const int L = L_nx;
     const int s_unit = SPARSE ? u % p.s_q : 0;
     const int s_row = SPARSE ? s_unit : (row_ok ? my_row / p.h_q : 0);
     const int W = p.causal ? min(max(L - p.s_q + 1 + s_row, 0), L) : L;
     const int Wunit = (SPARSE && p.causal) ? min(max(L - p.s_q + 1 + s_unit, 0), L) : L;
     const int W_lo = p.causal ? min(max(L - p.s_q + 1, 0), L) : L;   // every row sees keys < W_lo
     const int32_t* idx_row = SPARSE ? p.indices + (size_t)u * p.topk : nullptr;
-    const int s_begin = 2 * jb;
-    const int s_end = 2 * je;   // at least s_begin + 2
     const int pos_end = kPage * je;
     int tab_base = kPage * jb;
-    if (SPARSE) fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
 
-    // Q^T for this wave's k-steps: lane holds row l % 16, dims
-    // 32 ks + 8 (l / 16) .. + 7; a missing fifth k-step is zero.
-    bf16x8 qf[kQKSteps];
+    // Q^T for all 18 k-steps: lane holds row l % 16, dims 32 ks + 8 (l / 16)
+    // .. + 7.  Issued first: it depends on u only.
+    bf16x8 qf[kKSteps];
     {
       const int ln = opaque_lane();
       const int r = row_base + (ln & 15);
       const uint8_t* qrow = p.q + ((size_t)u * p.R + (r < p.R ? r : 0)) * (2 * kDqk) + 16 * (ln >> 4);
 #pragma unroll
-      for (int i = 0; i < kQKSteps; ++i) {
-        u32x4 v = *(const u32x4*)(qrow + 64 * (ks0 + min(i, nks - 1)));
-        if (r >= p.R || i >= nks) v = u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        u32x4 v = *(const u32x4*)(qrow + 64 * ks);
+        if (r >= p.R) v = u32x4{0, 0, 0, 0};
         if (qneg) v ^= 0x80008000u;   // exact bf16 negation
-        qf[i] = __builtin_bit_cast(bf16x8, v);
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
+    if (SPARSE) fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, G::kTabN), Wunit, idx_row);
+    // Dense: lane i holds the page of block pb + i.
+    int pb = jb;
+    int pages_v = 0;
+    if (!SPARSE) {
+      const int jl = jb + lane;
+      pages_v = (jl < je && jl * kPage < L) ? p.block_table[(size_t)b * p.max_blocks + jl] : 0;
+    }
+    // The next unit's length and blocks, through the scalar cache; the
+    // barrier below waits for them with everything else.
+    if (u < u1) {
+      n_nx = unit_blocks[u + 1];
+      L_nx = p.seqlens[SPARSE ? (u + 1) / p.s_q : u + 1];
+    }
     wait_vmem<0>();
-    lds_barrier();   // tab complete
+    lds_barrier();   // Q, page list and tab complete
+
+    // The unit's first page.
+    auto page_at = [&](int j) -> int {
+      if (SPARSE) return 0;
+      if (j - pb >= 64) {   // past the lanes' page list: reload it
+        pb = j;
+        const int jl = pb + lane;
+        pages_v = (jl < je && jl * kPage < L) ? p.block_table[(size_t)b * p.max_blocks + jl] : 0;
+      }
+      return __builtin_amdgcn_readlane(pages_v, j - pb);
+    };
+    uint64_t vis_cur = copy_page<FMT, SPARSE>(p, tab, tab_base, slot0, jb, L, page_at(jb));
+    uint64_t vis_next = 0;
 
     float m_run = -INFINITY;
     float l_part = 0.f;
@@ -175,99 +203,71 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
 #pragma unroll
     for (int d = 0; d < kDimTiles; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Slices s_begin .. s_begin + NS - 2 (slice s in slot (s - s_begin) % NS).
-    uint32_t vis[4];
-    vis[0] = copy_slice<FMT, SPARSE>(p, tab, tab_base, ring0, s_begin, L, true,
-                                     SPARSE ? 0 : page_of(p, b, s_begin >> 1, L));
-    vis[1] = copy_slice<FMT, SPARSE>(p, tab, tab_base, ring1, s_begin + 1, L, true,
-                                     SPARSE ? 0 : page_of(p, b, (s_begin + 1) >> 1, L));
-    vis[2] = 0u;
-    vis[3] = 0u;
-    if (NS == 4)
-      vis[2] = copy_slice<FMT, SPARSE>(p, tab, tab_base, ring2, s_begin + 2, L, s_begin + 2 < s_end,
-                                       SPARSE ? 0 : page_of(p, b, min(s_begin + 2, s_end - 1) >> 1, L));
-    int page_pf = SPARSE ? 0 : page_of(p, b, min(s_begin + NS - 1, s_end - 1) >> 1, L);
-    wait_vmem<(NS - 2) * G::kPerWave>();   // slice s_begin
-    lds_barrier();
-
-    int sl = s_begin;
-    auto step = [&](auto slot) __attribute__((always_inline)) {
-      constexpr int C = decltype(slot)::value;
-      constexpr int F = (C + NS - 1) % NS;   // slot of slice sl - 1
-      uint8_t* const rcur = C == 0 ? ring0 : (C == 1 ? ring1 : (C == 2 ? ring2 : ring3));
-      uint8_t* const rfree = F == 0 ? ring0 : (F == 1 ? ring1 : (F == 2 ? ring2 : ring3));
-      const uint32_t vmask = vis[C];
-      const int key0 = sl * kSlice;
-      uint8_t* const xcur = xs + (sl & 1) * (kWaves * kXchgBytes);
-      const uint8_t* kb = rcur;
-      if constexpr (FMT == 1) {
-        lds_barrier();   // every wave is done with the previous slice in kbf
-        if (vmask != 0u) dequant_slice<kThreads>(rcur, kbf);
-        lds_barrier();   // kbf holds slice sl
-        kb = kbf;
-      }
-      // ---- partial S^T = K Q^T over this wave's k-steps; tile kt covers
-      // keys 16 kt + 0..15: lane holds key 16 kt + l % 16 (A) and row
-      // l % 16 (B), dims 32 ks + 8 (l / 16) .. + 7.
-      f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (vmask != 0u) {
-        const int ln = opaque_lane();
-        const int t0 = ln & 15;
-        const int gg = ln >> 4;
-#pragma unroll
-        for (int i = 0; i < kQKSteps; ++i) {
-          const int c = 4 * (ks0 + min(i, nks - 1)) + gg;   // chunk (a zero Q step re-reads the last one)
-          const bf16x8 a0 = *(const bf16x8*)(kb + slice_off(t0, c));
-          const bf16x8 a1 = *(const bf16x8*)(kb + slice_off(16 + t0, c));
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[i], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[i], s1, 0, 0, 0);
-        }
-        *(f32x4*)(xcur + wave * kXchgBytes + lane * 16) = s0;
-        *(f32x4*)(xcur + wave * kXchgBytes + 1024 + lane * 16) = s1;
-      }
-      wait_vmem<(NS - 3) * G::kPerWave>();   // this wave's share of slice sl + 1
-      lds_barrier();   // partial tiles and slice sl + 1 visible; slot of sl - 1 free
-      // ---- copy slice sl + NS - 1 into the slot of slice sl - 1.
-      {
-        const bool more = sl + NS - 1 < s_end;
-        if (SPARSE && more) {
-          const int pos = kSlice * (sl + NS - 1);
-          if (pos - tab_base >= kTab) {   // the unit's range outgrew the table
+    auto step = [&](auto slot_c, int j) __attribute__((always_inline)) {
+      constexpr int C = decltype(slot_c)::value;
+      uint8_t* const rcur = C == 0 ? slot0 : slot1;
+      uint8_t* const rnext = C == 0 ? slot1 : slot0;
+      wait_vmem<0>();
+      lds_barrier();   // page j visible; the other slot (page j - 1) free
+      // ---- copy page j + 1 into the other slot.
+      if (j + 1 < je) {
+        if (SPARSE) {
+          const int pos = kPage * (j + 1);
+          if (pos + kPage - tab_base > G::kTabN) {   // the unit's range outgrew the table
             tab_base = pos;
-            fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
+            fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, G::kTabN), Wunit, idx_row);
+            wait_vmem<0>();
             lds_barrier();
           }
         }
-        vis[F] = copy_slice<FMT, SPARSE>(p, tab, tab_base, rfree, sl + NS - 1, L, more, page_pf);
-        if (!SPARSE) page_pf = page_of(p, b, min(sl + NS, s_end - 1) >> 1, L);
+        vis_next = copy_page<FMT, SPARSE>(p, tab, tab_base, rnext, j + 1, L, page_at(j + 1));
       }
-      const int cur_sl = sl;
-      ++sl;
+      const uint64_t vmask = vis_cur;
+      vis_cur = vis_next;
+      const uint8_t* kb = rcur;
+      if constexpr (FMT == 1) {
+        if (vmask != 0u) {
+          dequant_slice<kThreads>(rcur, kbf);
+          dequant_slice<kThreads>(rcur + kSlice * kFp8RowBytes, kbf + kSliceBytes);
+        }
+        lds_barrier();   // kbf holds page j
+        kb = kbf;
+      }
       if (vmask == 0u) return;
-      // ---- S^T = sum of the four partial tiles, in wave order.
-      float sv[8];
+      // ---- S^T tile of keys 16 wave .. + 15 (half wave >> 1 of the page,
+      // keys 16 (wave & 1) + l % 16) over all 18 k-steps.
       {
-        f32x4 a0 = *(const f32x4*)(xcur + lane * 16);
-        f32x4 a1 = *(const f32x4*)(xcur + 1024 + lane * 16);
+        const uint8_t* kh = kb + (wave >> 1) * kSliceBytes;
+        const int ln = opaque_lane();
+        const int t = 16 * (wave & 1) + (ln & 15);
+        const int gg = ln >> 4;
+        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-          a0 += *(const f32x4*)(xcur + w * kXchgBytes + lane * 16);
-          a1 += *(const f32x4*)(xcur + w * kXchgBytes + 1024 + lane * 16);
+        for (int ks = 0; ks < kKSteps; ks += 2) {
+          const bf16x8 a0 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + gg));
+          const bf16x8 a1 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + 4 + gg));
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], sb, 0, 0, 0);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sv[r] = a0[r];
-          sv[4 + r] = a1[r];
-        }
+        *(f32x4*)(xs + wave * 1024 + lane * 16) = sa + sb;
       }
-      // ---- mask + online softmax (exp2 domain, logit = sc * s).  Lane
-      // holds row l % 16 and keys 16 (i >> 2) + 4 g + (i & 3), i = 0..7.
-      const bool full = SPARSE ? (vmask == 0xFFFFFFFFu) : (cur_sl * kSlice + kSlice <= W_lo);
-      uint32_t okbits = 0xFFu;
+      lds_barrier();   // all four S^T tiles visible
+      // ---- lane holds row l % 16 and keys 16 w + 4 g + i (i < 4) for w < 4.
+      float sv[16];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const f32x4 a = *(const f32x4*)(xs + w * 1024 + lane * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[4 * w + i] = a[i];
+      }
+      // ---- mask + online softmax (exp2 domain, logit = sc * s).
+      const int key0 = kPage * j;
+      const bool full = SPARSE ? (vmask == ~0ull) : (key0 + kPage <= W_lo);
+      uint32_t okbits = 0xFFFFu;
       if (!full) {
         okbits = 0u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 16; ++i) {
           const int tl = 16 * (i >> 2) + 4 * g + (i & 3);
           const bool ok = SPARSE ? ((vmask >> tl) & 1u) != 0u : (key0 + tl < W);
           okbits |= ok ? (1u << i) : 0u;
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[i]);
       mx = fmaxf(mx, xor16(mx));
       mx = fmaxf(mx, xor32(mx));
       mx = mx == -INFINITY ? -INFINITY : mx * sc;
@@ -290,23 +290,27 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
         for (int d = 0; d < kDimTiles; ++d) o[d] *= alpha;
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float e[8];
+      float e[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -m_use));
+      for (int i = 0; i < 16; ++i) e[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -m_use));
       if (!full) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = ((okbits >> i) & 1u) ? e[i] : 0.f;
+        for (int i = 0; i < 16; ++i) e[i] = ((okbits >> i) & 1u) ? e[i] : 0.f;
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) l_part += e[i];
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
-                                                         pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])});
-      // ---- O^T += V^T P^T for V dims 128 wave + 16 dt .. + 15.  k-slot i
-      // of lane group g is key 4 g + i (i < 4) or 16 + 4 g + i - 4; the
+      for (int i = 0; i < 16; ++i) l_part += e[i];
+      // ---- O^T += V^T P^T over the two halves of the page.  PV k-step h
+      // covers key tiles 2 h and 2 h + 1: k-slot i of lane group g is key
+      // 4 g + i of tile 2 h (i < 4) or of tile 2 h + 1 (i >= 4); the
       // transposed read of 16-lane group G takes keys 4 G + (j >> 2) (+ 16
-      // for the second read) and dims 4 (j & 3) .. + 3 of the tile, i.e.
-      // chunk 16 wave + 2 dt + ((j >> 1) & 1).
-      {
+      // for the second read) and dims 4 (j & 3) .. + 3 of the dim tile, i.e.
+      // chunk 16 wave + 2 dt + ((j >> 1) & 1) of the half.
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 pb = __builtin_bit_cast(
+            bf16x8, u32x4{pack_bf16x2(e[8 * h + 0], e[8 * h + 1]), pack_bf16x2(e[8 * h + 2], e[8 * h + 3]),
+                          pack_bf16x2(e[8 * h + 4], e[8 * h + 5]), pack_bf16x2(e[8 * h + 6], e[8 * h + 7])});
+        const uint8_t* vh = kb + h * kSliceBytes;
         const int ln = opaque_lane();
         const int jj = ln & 15;
         const int tA = 4 * (ln >> 4) + (jj >> 2);
@@ -315,8 +319,8 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
 #pragma unroll
         for (int dt = 0; dt < kDimTiles; ++dt) {
           const int c = 16 * wave + 2 * dt + ((jj >> 1) & 1);
-          const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + slice_off(tA, c) + xo));
-          const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + slice_off(tB, c) + xo));
+          const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + slice_off(tA, c) + xo));
+          const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + slice_off(tB, c) + xo));
           const u32x2 xa = __builtin_bit_cast(u32x2, va);
           const u32x2 xb = __builtin_bit_cast(u32x2, vb);
           const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{xa[0], xa[1], xb[0], xb[1]});
@@ -324,16 +328,12 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
         }
       }
     };
-    while (sl < s_end) {
-      step(Slot<0>{});
-      if (sl >= s_end) break;
-      step(Slot<1>{});
-      if (sl >= s_end) break;
-      step(Slot<2>{});
-      if constexpr (NS == 4) {
-        if (sl >= s_end) break;
-        step(Slot<3>{});
-      }
+    int j = jb;
+    while (j < je) {
+      step(Slot<0>{}, j);
+      if (++j >= je) break;
+      step(Slot<1>{}, j);
+      ++j;
     }
 
     // ---- epilogue: lane holds row l % 16, dims 128 wave + 16 dt + 4 g +
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
       }
     }
     wait_vmem<0>();
-    lds_barrier();   // the next unit refills the table and the ring
+    lds_barrier();   // the next unit refills the table and the slots
   }
 }
 

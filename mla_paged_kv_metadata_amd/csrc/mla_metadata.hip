@@ -19,6 +19,8 @@
 // the sequence, so trailing masked entries cost nothing; one wave per unit),
 // the total cost, then the units in chunks of 1024 with two workgroup scans
 // each.  The part rows are assembled in LDS and written out at the end.
+// Besides its range, a part row carries the length and block count of its
+// first unit, so that the decode can start that unit without reading them.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -140,7 +142,11 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
     const int u = base + tid;
     const bool live = u < units;
     long long nb = 0;
-    if (live) nb = SPARSE ? unit_blocks[u] : dense_unit_blocks(seqlens[u]);
+    int Lu = 0;
+    if (live) {
+      Lu = seqlens[SPARSE ? u / s_q : u];
+      nb = SPARSE ? unit_blocks[u] : dense_unit_blocks(Lu);
+    }
     const long long c = live ? nb + c0 : 0;
     long long chunk_c, chunk_k;
     const long long Cu = carry_c + wg_exclusive_scan(c, sh[1], &chunk_c);
@@ -161,6 +167,8 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
         row[0] = u;
         row[1] = (int32_t)(p == f ? 0 : p * T - Cu - c0);
         row[4] = (int32_t)(p - f);
+        row[5] = Lu;
+        row[6] = (int32_t)nb;
       }
       // Parts whose last unit is u: those the next unit does not start in.
       const long long hi = (u + 1 < units) ? min(l, (Cu + c + c0) / T - 1) : l;

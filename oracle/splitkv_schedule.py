@@ -24,9 +24,13 @@ the schedule this project defines for them:
 The device arrays:
   tile_metadata = header[8] + P rows of 8 int32 + U int32
     header = [P, T, c0, U, total_blocks, 0x4D4C4131, 0, 0]
-    row p  = [u_first, j_first, u_last, j_end, split_of_u_first, 0, 0, 0]
+    row p  = [u_first, j_first, u_last, j_end, split_of_u_first,
+              L_first, n_first, 0]
              (j_end is one past the last block of u_last in the part;
-              an empty part is [-1, 0, -1, 0, 0, 0, 0, 0])
+              L_first is cache_seqlens of u_first's sequence and n_first its
+              block count n_{u_first}, carried so that a part can start its
+              first unit without reading them; an empty part is
+              [-1, 0, -1, 0, 0, 0, 0, 0])
     then n_u for every unit
   num_splits = U + 1 int32 prefix sums of k_u, the number of parts unit u
                is spread over.
@@ -61,8 +65,9 @@ def unit_blocks_sparse(seqlens, indices) -> np.ndarray:
     return np.array(out, dtype=np.int64)
 
 
-def schedule(n_blocks, num_parts: int, c0: int):
-    """Return (tile_metadata int32 array, num_splits int32 array)."""
+def schedule(n_blocks, num_parts: int, c0: int, unit_len=None):
+    """Return (tile_metadata int32 array, num_splits int32 array).
+    unit_len[u] is the cache length of unit u's sequence (0 if not given)."""
     n_blocks = [int(x) for x in n_blocks]
     U = len(n_blocks)
     P = int(num_parts)
@@ -98,7 +103,8 @@ def schedule(n_blocks, num_parts: int, c0: int):
         u0, j0 = members[p][0]
         u1, j1 = members[p][-1]
         split = parts_of_unit[u0].index(p)
-        r[:] = [u0, j0, u1, j1 + 1, split, 0, 0, 0]
+        L0 = int(unit_len[u0]) if unit_len is not None else 0
+        r[:] = [u0, j0, u1, j1 + 1, split, L0, n_blocks[u0], 0]
     return md, num_splits
 
 
@@ -117,6 +123,7 @@ def check_schedule(md, num_splits, n_blocks):
         if u0 < 0:
             continue
         assert u0 <= u1
+        assert int(md[HEADER + ROW * p + 6]) == int(n_blocks[u0])
         for u in range(u0, u1 + 1):
             jb = j0 if u == u0 else 0
             je = j1 if u == u1 else int(n_blocks[u])

@@ -95,7 +95,7 @@ def test_schedule_matches_oracle_bitwise():
         from mla_paged_kv_metadata_amd import get_mla_metadata
         md = get_mla_metadata(slt, s_q * 16, 1, s_q=s_q, indices=idx, num_parts=P)
         T.cuda.synchronize()
-        ref_md, ref_ns = S.schedule(nb, P, 2)
+        ref_md, ref_ns = S.schedule(nb, P, 2, unit_len=np.repeat(sl, s_q) if sparse else sl)
         assert np.array_equal(md.tile_metadata.cpu().numpy(), ref_md), trial
         assert np.array_equal(md.num_splits.cpu().numpy(), ref_ns), trial
         S.check_schedule(ref_md, ref_ns, nb)
