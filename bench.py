@@ -15,14 +15,31 @@ bf16 TFLOPS under "mtp"; the FP8 and sparse workloads under "fp8"/"sparse".
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Three physical copies of each page pool (same logical cache, pages shuffled
 differently) are used in rotation so that consecutive steps do not hit the
-256 MB Infinity Cache.  Kernel times come from HIP events recorded on the
-launch stream around each kernel inside the timed loop.
+256 MB Infinity Cache.
+
+Two timed loops per workload:
+  * the step as a HIP graph (one graph per pool copy, captured once and
+    replayed), as a serving loop runs it; its wall time per step gives
+    `value` / `ms_per_step`.  Its outputs are checked bit for bit against
+    an eager run first.
+  * the same step launched eagerly with HIP events recorded on the launch
+    stream around each kernel; the split-KV kernel's mean event time gives
+    the roofline's `achieved` (algorithmic bytes or flops per launch over it).
+`roofline.traffic` (measured HBM bytes per launch) is read from the
+committed counter summary in profiles/ when it was taken on the kernel
+sources as they are now, else null.
+
+    python bench.py --pmc-run
+
+runs the workload that the counter summaries are taken on: a plain fp32
+copy of known size (the counters' calibration), then a few eager steps.
 
 Prints ONE JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -107,6 +124,53 @@ class Workload:
         if ev is not None:
             ev[3].record()
 
+    def capture(self):
+        """One HIP graph per pool copy holding the whole step."""
+        import torch
+        import mla_paged_kv_metadata_amd as m
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(2 * len(self.calls)):
+                self.step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graphs = []
+        for c in self.calls:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                m.refresh_mla_metadata(self.md, self.seqlens, self.indices)
+                c.partial()
+                c.combine()
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def check_graph(self):
+        """Each graph's out/lse must equal the eager step's, bit for bit."""
+        import torch
+        c0 = self.calls[0]
+        for r, g in enumerate(self.graphs):
+            self.step(r)
+            torch.cuda.synchronize()
+            ref_o, ref_l = c0.out.clone(), c0.lse.clone()
+            c0.out.fill_(0)
+            c0.lse.fill_(0)
+            g.replay()
+            torch.cuda.synchronize()
+            if not (torch.equal(c0.out, ref_o) and torch.equal(c0.lse, ref_l)):
+                raise RuntimeError(f"graph replay {r} differs from the eager step")
+
+    def time_graph(self, steps: int, warmup: int) -> float:
+        import torch
+        for i in range(warmup):
+            self.graphs[i % len(self.graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.graphs[i % len(self.graphs)].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
     def time(self, steps: int, warmup: int) -> dict:
         import torch
         for i in range(warmup):
@@ -163,6 +227,75 @@ def cpu_baseline(inp, target_s: float) -> dict:
                       f"({kv / 1e6:.1f} MB of KV rows), {dt:.1f} s"}
 
 
+# The dominant kernel of each workload, as rocprofv3 names it, and the
+# sources it is built from (the counter summary is valid while they match).
+KERNEL_NAMES = {
+    1: "void mla::narrow::narrow_kernel<0, false>(mla::DecodeParams)",
+    2: "void mla::wide::offset_kernel(mla::DecodeParams)",
+    3: "void mla::wide::wide_kernel<1, false>(mla::DecodeParams)",
+    4: "void mla::wide::wide_kernel<1, true>(mla::DecodeParams)",
+}
+KERNEL_SOURCES = {
+    1: ["mla_decode_narrow.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "narrow_kernel_membound_b64_h16_traffic.md")
+
+
+def sources_sha(cfg_idx: int) -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mla_paged_kv_metadata_amd", "csrc")
+    for f in KERNEL_SOURCES[cfg_idx]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg_idx: int):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (a line `traffic-json: {...}`), or None if there is none or it
+    was taken on other kernel sources."""
+    if cfg_idx not in KERNEL_SOURCES or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if line.startswith("traffic-json:"):
+                d = json.loads(line.split(":", 1)[1])
+                if d.get("sources_sha") != sources_sha(cfg_idx):
+                    return None
+                return d
+    return None
+
+
+def pmc_run():
+    """The run the counter summaries are taken on: a plain copy of known size
+    (fp32, 256 Mi elements: 1 GiB read, 1 GiB written), then eager steps of
+    the memory-bound workload."""
+    import torch
+    n = 256 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)   # one elementwise kernel: reads n*4 B, writes n*4 B
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    w = Workload(1, 3)
+    for i in range(6):
+        w.step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] pmc run done: copy of {n * 4} B x3, 6 steps of {w.cfg.name}")
+
+
+def run_workload(idx: int, replicas: int, steps: int, warmup: int):
+    import torch
+    w = Workload(idx, replicas)
+    w.capture()
+    w.check_graph()
+    t = w.time(steps, warmup)
+    t["graph_ms_per_step"] = w.time_graph(steps, warmup)
+    return w, t
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +308,8 @@ def main():
                     help="skip the MTP, FP8 and sparse workloads")
     ap.add_argument("--only", choices=["mtp", "fp8", "sparse"], default=None,
                     help="time just this secondary workload (for profiling)")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="the run hardware counters are collected on (no timing)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -187,21 +322,24 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.pmc_run:
+        pmc_run()
+        return
 
     if args.only is not None:
         idx = {"mtp": 2, "fp8": 3, "sparse": 4}[args.only]
-        w = Workload(idx, args.replicas)
-        t = w.time(args.steps, args.warmup)
+        w, t = run_workload(idx, args.replicas, args.steps, args.warmup)
         print(json.dumps({"workload": w.cfg.name, "timing_ms": t,
                           "splitkv_tflops": w.flops / (t["splitkv_ms"] * 1e-3) / 1e12}), flush=True)
         return
 
-    prim = Workload(1, args.replicas)
-    log("[bench] timing membound")
-    tm = prim.time(args.steps, args.warmup)
+    prim, tm = run_workload(1, args.replicas, args.steps, args.warmup)
+    log("[bench] membound timed")
     kv = prim.bytes["kv"]
-    value = kv / (tm["wall_ms_per_step"] * 1e-3) / 1e9
+    step_ms = tm["graph_ms_per_step"]
+    value = kv / (step_ms * 1e-3) / 1e9
     achieved = prim.bytes["total"] / (tm["splitkv_ms"] * 1e-3) / 1e9
+    traffic = measured_traffic(1)
     result = {
         "metric": "MLA paged decode: KV-read GB/s (h_q=16) and bf16 TFLOPS (h_q=128,s_q=2)",
         "value": round(value, 1),
@@ -209,7 +347,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(tm["wall_ms_per_step"], 5),
+        "ms_per_step": round(step_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -222,36 +360,42 @@ def main():
             "sum_seqlens": int(prim.inp.seqlens.sum()),
             "kv_bytes": kv, "kv_format": "bf16", "page_size": 64,
             "num_parts": prim.md.num_parts, "pool_replicas": args.replicas,
+            "step": "HIP graph replay of metadata + split-KV + combine",
         },
         "timing_ms": {k: round(v, 5) for k, v in tm.items()},
         "roofline": {
-            "kernel": "splitkv_kernel",
+            "kernel": KERNEL_NAMES[1],
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else int(traffic["bytes_per_launch"]),
             "algorithmic_bytes": prim.bytes["total"],
         },
     }
+    if traffic is not None:
+        result["roofline"]["traffic_detail"] = {k: traffic[k] for k in
+                                                ("fetch_bytes", "write_bytes", "fetch_factor", "write_factor")
+                                                if k in traffic}
     if not args.only_primary:
         extra = {}
         for idx, key in ((2, "mtp"), (3, "fp8"), (4, "sparse")):
             del prim
             torch.cuda.empty_cache()
-            w = Workload(idx, args.replicas)
             log(f"[bench] timing {key}")
-            t = w.time(max(10, args.steps // 2), args.warmup)
-            step_s = t["wall_ms_per_step"] * 1e-3
+            w, t = run_workload(idx, args.replicas, max(10, args.steps // 2), args.warmup)
+            step_s = t["graph_ms_per_step"] * 1e-3
             extra[key] = {
                 "workload": w.cfg.name,
-                "ms_per_step": round(t["wall_ms_per_step"], 5),
+                "ms_per_step": round(t["graph_ms_per_step"], 5),
                 "tflops": round(w.flops / step_s / 1e12, 2),
                 "kv_gbs": round(w.bytes["kv"] / step_s / 1e9, 1),
+                "splitkv_kernel": KERNEL_NAMES[idx],
                 "splitkv_ms": round(t["splitkv_ms"], 5),
                 "combine_ms": round(t["combine_ms"], 5),
                 "metadata_ms": round(t["metadata_ms"], 5),
+                "eager_ms_per_step": round(t["wall_ms_per_step"], 5),
                 "splitkv_tflops": round(w.flops / (t["splitkv_ms"] * 1e-3) / 1e12, 2),
                 "mfma_frac_of_bf16_peak": round(w.flops / (t["splitkv_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                 "flops": w.flops,
