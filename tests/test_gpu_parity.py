@@ -195,3 +195,30 @@ def test_sparse_topk_beyond_table(oracle_mod, fmt):
         ro, rl = oracle_mod.decode(inp)
         compare(o, l, ro, rl, fmt, f"sparse topk=2500 fmt={fmt} parts={parts}")
 
+
+
+@pytest.mark.parametrize("h_q,s_q,causal", [(16, 1, False), (128, 2, True), (128, 1, False)])
+def test_scores_growing_along_the_sequence(oracle_mod, h_q, s_q, causal):
+    """Scores that rise by about 0.75 per key (hundreds of log2 units over
+    the sequence): the running maximum is overtaken again and again, which
+    exercises the rescaling of the 16-row kernel and the second pass of the
+    128-row dense kernel."""
+    seqlens = [320, 70, 1000]
+    cfg = gen.small_config(len(seqlens), s_q, h_q, seqlens, causal=causal, seed=4242 + h_q)
+    inp = gen.make_inputs(cfg, poison=True)
+    rng = np.random.default_rng(7)
+    # q = 1 on every dim (with a little noise); key t of sequence b gets
+    # t / 32 added on every dim, so its score grows by about 0.75 per key.
+    qf = 1.0 + 0.05 * rng.standard_normal(inp.q.shape).astype(np.float32)
+    inp.q[...] = gen.f32_to_bf16_bits(qf)
+    rows = inp.kcache.view(np.uint16).reshape(inp.kcache.shape[0], 64, 576)
+    for b, L in enumerate(seqlens):
+        for t in range(L):
+            page = int(inp.block_table[b, t // 64])
+            k = gen.bf16_bits_to_f32(rows[page, t % 64]) * 0.2 + t / 32.0
+            rows[page, t % 64] = gen.f32_to_bf16_bits(k.astype(np.float32))
+    log(f"growing scores h_q={h_q} s_q={s_q} causal={causal}")
+    o, l, _ = run_gpu(inp, num_parts=8)
+    ro, rl = oracle_mod.decode(inp)
+    assert rl.max() - rl.min() > 100, "the test needs widely spread scores"
+    compare(o, l, ro, rl, inp.fmt, "growing scores")
