@@ -29,10 +29,11 @@ Two timed loops per workload:
 committed counter summary in profiles/ when it was taken on the kernel
 sources as they are now, else null.
 
-    python bench.py --pmc-run
+    python bench.py --pmc-run [membound|mtp|fp8|sparse]
 
-runs the workload that the counter summaries are taken on: a plain fp32
-copy of known size (the counters' calibration), then a few eager steps.
+runs the workload that the counter summaries are taken on: for the
+memory-bound one a plain fp32 copy of known size first (the counters'
+calibration), then a few eager steps.
 
 Prints ONE JSON line.
 """
@@ -231,14 +232,23 @@ def cpu_baseline(inp, target_s: float) -> dict:
 # sources it is built from (the counter summary is valid while they match).
 KERNEL_NAMES = {
     1: "void mla::narrow::narrow_kernel<0, false>(mla::DecodeParams)",
-    2: "void mla::wide::offset_kernel(mla::DecodeParams)",
+    2: "mla::wide::offset_kernel(mla::DecodeParams)",
     3: "void mla::wide::wide_kernel<1, false>(mla::DecodeParams)",
     4: "void mla::wide::wide_kernel<1, true>(mla::DecodeParams)",
 }
 KERNEL_SOURCES = {
     1: ["mla_decode_narrow.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+    2: ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+    3: ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+    4: ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "narrow_kernel_membound_b64_h16_traffic.md")
+# Kernel trace + MFMA counter summaries of the compute-bound workloads.
+MFMA_FILES = {
+    2: os.path.join(ROOT, "profiles", "offset_kernel_mtp_b128_sq2_h128_kernel_stats.md"),
+    3: os.path.join(ROOT, "profiles", "wide_kernel_fp8_b64_h128_L8192_kernel_stats.md"),
+    4: os.path.join(ROOT, "profiles", "wide_kernel_sparse_b32_h128_top2048_kernel_stats.md"),
+}
 
 
 def sources_sha(cfg_idx: int) -> str:
@@ -254,36 +264,52 @@ def measured_traffic(cfg_idx: int):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary (a line `traffic-json: {...}`), or None if there is none or it
     was taken on other kernel sources."""
-    if cfg_idx not in KERNEL_SOURCES or not os.path.exists(TRAFFIC_FILE):
+    if cfg_idx != 1:
         return None
-    with open(TRAFFIC_FILE) as fh:
+    return _summary_json(TRAFFIC_FILE, "traffic-json", cfg_idx)
+
+
+def _summary_json(path: str, tag: str, cfg_idx: int):
+    """The `tag: {...}` line of a committed counter summary, or None if there
+    is none or it was taken on other kernel sources."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
         for line in fh:
-            if line.startswith("traffic-json:"):
+            if line.startswith(tag + ":"):
                 d = json.loads(line.split(":", 1)[1])
-                if d.get("sources_sha") != sources_sha(cfg_idx):
-                    return None
-                return d
+                return d if d.get("sources_sha") == sources_sha(cfg_idx) else None
     return None
 
 
-def pmc_run():
-    """The run the counter summaries are taken on: a plain copy of known size
-    (fp32, 256 Mi elements: 1 GiB read, 1 GiB written), then eager steps of
-    the memory-bound workload."""
+def measured_mfma(cfg_idx: int):
+    """MFMA counter figures (MfmaUtil, MFMA flops) of the dominant kernel from
+    the committed summary, or None."""
+    return _summary_json(MFMA_FILES[cfg_idx], "mfma-json", cfg_idx) if cfg_idx in MFMA_FILES else None
+
+
+def pmc_run(which: str):
+    """The run the counter summaries are taken on: for the memory-bound
+    workload, first a plain copy of known size (fp32, 256 Mi elements: 1 GiB
+    read, 1 GiB written: the counters' calibration), then six eager steps of
+    the workload."""
     import torch
-    n = 256 * 1024 * 1024
-    src = torch.ones(n, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        torch.mul(src, 1.0, out=dst)   # one elementwise kernel: reads n*4 B, writes n*4 B
-    torch.cuda.synchronize()
-    del src, dst
-    torch.cuda.empty_cache()
-    w = Workload(1, 3)
+    idx = {"membound": 1, "mtp": 2, "fp8": 3, "sparse": 4}[which]
+    if idx == 1:
+        n = 256 * 1024 * 1024
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)   # one elementwise kernel: reads n*4 B, writes n*4 B
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+        log(f"[bench] copy of {n * 4} B x3")
+    w = Workload(idx, 3)
     for i in range(6):
         w.step(i)
     torch.cuda.synchronize()
-    log(f"[bench] pmc run done: copy of {n * 4} B x3, 6 steps of {w.cfg.name}")
+    log(f"[bench] pmc run done: 6 steps of {w.cfg.name} ({w.flops} flops per split-KV launch)")
 
 
 def run_workload(idx: int, replicas: int, steps: int, warmup: int):
@@ -308,7 +334,8 @@ def main():
                     help="skip the MTP, FP8 and sparse workloads")
     ap.add_argument("--only", choices=["mtp", "fp8", "sparse"], default=None,
                     help="time just this secondary workload (for profiling)")
-    ap.add_argument("--pmc-run", action="store_true",
+    ap.add_argument("--pmc-run", nargs="?", const="membound", default=None,
+                    choices=["membound", "mtp", "fp8", "sparse"],
                     help="the run hardware counters are collected on (no timing)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -323,7 +350,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     if args.pmc_run:
-        pmc_run()
+        pmc_run(args.pmc_run)
         return
 
     if args.only is not None:
@@ -398,6 +425,7 @@ def main():
                 "eager_ms_per_step": round(t["wall_ms_per_step"], 5),
                 "splitkv_tflops": round(w.flops / (t["splitkv_ms"] * 1e-3) / 1e12, 2),
                 "mfma_frac_of_bf16_peak": round(w.flops / (t["splitkv_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "rocprof": measured_mfma(idx),
                 "flops": w.flops,
                 "kv_bytes": w.bytes["kv"],
             }
