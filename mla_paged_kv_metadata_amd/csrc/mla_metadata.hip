@@ -60,24 +60,43 @@ __device__ __forceinline__ long long wg_exclusive_scan(long long v, long long* s
   return before + incl - v;
 }
 
-// Blocks of 64 keys that sparse unit u spans.  One wave.
+// Blocks of 64 keys that sparse unit u spans.  One wave; the index row is
+// read in batches of eight loads per lane, all issued before any is used.
 __device__ __forceinline__ int sparse_unit_blocks(const int32_t* __restrict__ indices, int topk, int L,
                                                   int u, bool vec4, int lane) {
+  constexpr int kBatch = 8;
   const int32_t* idx = indices + (size_t)u * topk;
   int last = -1;
   if (vec4) {
     const int4* idx4 = (const int4*)idx;
-    for (int e4 = lane; 4 * e4 < topk; e4 += 64) {
-      const int4 t = idx4[e4];
-      if (t.x >= 0 && t.x < L) last = 4 * e4;
-      if (t.y >= 0 && t.y < L) last = 4 * e4 + 1;
-      if (t.z >= 0 && t.z < L) last = 4 * e4 + 2;
-      if (t.w >= 0 && t.w < L) last = 4 * e4 + 3;
+    const int n4 = topk / 4;
+    for (int base = 0; base < n4; base += 64 * kBatch) {
+      int4 t[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int e4 = base + lane + 64 * k;
+        t[k] = e4 < n4 ? idx4[e4] : make_int4(-1, -1, -1, -1);
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int e = 4 * (base + lane + 64 * k);
+        if (t[k].x >= 0 && t[k].x < L) last = max(last, e);
+        if (t[k].y >= 0 && t[k].y < L) last = max(last, e + 1);
+        if (t[k].z >= 0 && t[k].z < L) last = max(last, e + 2);
+        if (t[k].w >= 0 && t[k].w < L) last = max(last, e + 3);
+      }
     }
   } else {
-    for (int e = lane; e < topk; e += 64) {
-      const int t = idx[e];
-      if (t >= 0 && t < L) last = e;
+    for (int base = 0; base < topk; base += 64 * kBatch) {
+      int t[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int e = base + lane + 64 * k;
+        t[k] = e < topk ? idx[e] : -1;
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (t[k] >= 0 && t[k] < L) last = max(last, base + lane + 64 * k);
     }
   }
 #pragma unroll
@@ -122,8 +141,8 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
         cost += n + c0;
       }
     }
-    // The counts are read back by other waves below.
-    __threadfence();
+    // The counts are read back by other waves of this workgroup after the
+    // barrier in the scan below, which orders these stores before them.
   } else {
     for (int u = tid; u < units; u += kMdThreads) {
       const int n = dense_unit_blocks(seqlens[u]);
