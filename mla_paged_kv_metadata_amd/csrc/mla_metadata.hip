@@ -14,7 +14,8 @@
 // Every part thus receives at most T positions of work, and a unit is split
 // over the parts its blocks fall into.
 //
-// One 1024-thread workgroup does it all in a single launch: block counts
+// One 1024-thread workgroup does it all in a single launch (one wave for
+// up to 64 dense units): block counts
 // (for sparse units, up to one past the last index entry that lies inside
 // the sequence, so trailing masked entries cost nothing; one wave per unit),
 // the total cost, then the units in chunks of 1024 with two workgroup scans
@@ -217,11 +218,77 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
   for (int i = tid; i < P * kPartRow; i += kMdThreads) md[kHeader + i] = rows[i];
 }
 
+// Dense schedule for at most 64 units: one wave, one unit per lane, the
+// same arithmetic as metadata_kernel without its workgroup scans.
+__global__ __launch_bounds__(64) void metadata_wave_kernel(const int32_t* __restrict__ seqlens, int units,
+                                                          int num_parts, int32_t* __restrict__ md,
+                                                          int32_t* __restrict__ num_splits) {
+  __shared__ int32_t rows[kMaxParts * kPartRow];
+  const int lane = threadIdx.x;
+  const int P = num_parts;
+  const long long c0 = kUnitOverhead;
+  int32_t* unit_blocks = md + kHeader + kPartRow * P;
+  const bool live = lane < units;
+  const int Lu = live ? seqlens[lane] : 0;
+  for (int i = lane; i < P * kPartRow; i += 64) {
+    const int f = i & (kPartRow - 1);
+    rows[i] = (f == 0 || f == 2) ? -1 : 0;
+  }
+  const long long nb = live ? dense_unit_blocks(Lu) : 0;
+  if (live) unit_blocks[lane] = (int32_t)nb;
+  const long long c = live ? nb + c0 : 0;
+  const long long incl = wave_inclusive_scan(c, lane);
+  const long long tot_cost = __shfl(incl, 63);
+  const long long T = tot_cost > 0 ? (tot_cost + P - 1) / P : 1;
+  const long long Cu = incl - c;
+  long long f = 0, l = -1;
+  if (live) {
+    f = (Cu + c0) / T;
+    l = (Cu + c0 + nb - 1) / T;
+  }
+  const long long k = live ? l - f + 1 : 0;
+  const long long kincl = wave_inclusive_scan(k, lane);
+  __syncthreads();   // row defaults before the rows below
+  if (live) {
+    num_splits[lane + 1] = (int32_t)kincl;
+    const long long lo = lane > 0 ? max(f, (Cu - 1) / T + 1) : f;
+    for (long long pp = lo; pp <= l; ++pp) {
+      int32_t* row = rows + kPartRow * pp;
+      row[0] = lane;
+      row[1] = (int32_t)(pp == f ? 0 : pp * T - Cu - c0);
+      row[4] = (int32_t)(pp - f);
+      row[5] = Lu;
+      row[6] = (int32_t)nb;
+    }
+    const long long hi = (lane + 1 < units) ? min(l, (Cu + c + c0) / T - 1) : l;
+    for (long long pp = f; pp <= hi; ++pp) {
+      int32_t* row = rows + kPartRow * pp;
+      row[2] = lane;
+      row[3] = (int32_t)(pp == l ? nb : (pp + 1) * T - Cu - c0);
+    }
+  }
+  __syncthreads();
+  if (lane == 0) num_splits[0] = 0;
+  if (lane < kHeader) {
+    const int32_t v = lane == 0 ? P
+                      : lane == 1 ? (int32_t)T
+                      : lane == 2 ? (int32_t)c0
+                      : lane == 3 ? units
+                      : lane == 4 ? (int32_t)(tot_cost - c0 * units)
+                      : lane == 5 ? kMagic : 0;
+    md[lane] = v;
+  }
+  for (int i = lane; i < P * kPartRow; i += 64) md[kHeader + i] = rows[i];
+}
+
 hipError_t launch_metadata(const int32_t* seqlens, const int32_t* indices, int s_q, int topk,
                            int units, int num_parts, int32_t* md, int32_t* num_splits,
                            hipStream_t stream) {
   if (num_parts < 1 || num_parts > kMaxParts) return hipErrorInvalidValue;
-  if (indices == nullptr) {
+  if (indices == nullptr && units <= 64) {
+    hipLaunchKernelGGL(metadata_wave_kernel, dim3(1), dim3(64), 0, stream, seqlens, units, num_parts, md,
+                       num_splits);
+  } else if (indices == nullptr) {
     hipLaunchKernelGGL(metadata_kernel<false>, dim3(1), dim3(kMdThreads), 0, stream, seqlens, indices,
                        s_q, topk, 0, units, num_parts, md, num_splits);
   } else {
