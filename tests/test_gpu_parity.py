@@ -222,3 +222,17 @@ def test_scores_growing_along_the_sequence(oracle_mod, h_q, s_q, causal):
     ro, rl = oracle_mod.decode(inp)
     assert rl.max() - rl.min() > 100, "the test needs widely spread scores"
     compare(o, l, ro, rl, inp.fmt, "growing scores")
+
+
+@pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8])
+@pytest.mark.parametrize("parts,s_q", [(1, 1), (2, 2)])
+def test_narrow_pieces_longer_than_64_pages(oracle_mod, fmt, parts, s_q):
+    # 16 or 32 rows per sequence (the 16-row kernel) and one or two parts,
+    # so a part walks pieces of up to 141 pages: its per-lane page list is
+    # reloaded at 64 and 128 pages; 4160 keys is exactly 65 pages.
+    cfg = gen.small_config(3, s_q, 16, [9000, 4160, 33], causal=s_q > 1, fmt=fmt, seed=61 + parts)
+    inp = gen.make_inputs(cfg, poison=True, extra_pages=3)
+    log(f"narrow long pieces fmt={fmt} parts={parts} s_q={s_q}")
+    o, l, _ = run_gpu(inp, num_parts=parts)
+    ro, rl = oracle_mod.decode(inp)
+    compare(o, l, ro, rl, fmt, f"narrow long fmt={fmt} parts={parts} s_q={s_q}")
