@@ -18,10 +18,12 @@ differently) are used in rotation so that consecutive steps do not hit the
 256 MB Infinity Cache.
 
 Two timed loops per workload:
-  * the step as a HIP graph (one graph per pool copy, captured once and
-    replayed), as a serving loop runs it; its wall time per step gives
-    `value` / `ms_per_step`.  Its outputs are checked bit for bit against
-    an eager run first.
+  * the steps replayed from HIP graphs, as a serving loop runs them: one
+    graph holds a whole rotation of consecutive steps (one per pool copy,
+    each step complete: schedule, split-KV kernel, combine), so the launch
+    overhead of a graph is paid once per rotation; wall time per step gives
+    `value` / `ms_per_step`.  The graphs' outputs are checked bit for bit
+    against an eager step first.
   * the same step launched eagerly with HIP events recorded on the launch
     stream around each kernel; the split-KV kernel's mean event time gives
     the roofline's `achieved` (algorithmic bytes or flops per launch over it).
@@ -90,8 +92,10 @@ class Workload:
         self.q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to(dev)
         self.seqlens = torch.from_numpy(inp.seqlens).to(dev)
         self.indices = torch.from_numpy(inp.indices).to(dev) if inp.indices is not None else None
-        self.md = m.get_mla_metadata(self.seqlens, inp.s_q * inp.h_q, 1, s_q=inp.s_q,
-                                     indices=self.indices)
+        # One schedule buffer per pool copy (each step builds its own).
+        self.mds = [m.get_mla_metadata(self.seqlens, inp.s_q * inp.h_q, 1, s_q=inp.s_q,
+                                       indices=self.indices) for _ in range(replicas)]
+        self.md = self.mds[0]
         self.calls = []
         out = lse = ws = None
         for r in range(replicas):
@@ -102,7 +106,7 @@ class Workload:
             else:
                 k = torch.from_numpy(v.kcache).to(dev)
             bt = torch.from_numpy(v.block_table).to(dev)
-            c = m.DecodeCall(self.q, k, bt, self.seqlens, self.md, softmax_scale=inp.softmax_scale,
+            c = m.DecodeCall(self.q, k, bt, self.seqlens, self.mds[r], softmax_scale=inp.softmax_scale,
                              causal=inp.causal, indices=self.indices, out=out, lse=lse, workspace=ws)
             out, lse, ws = c.out, c.lse, c.workspace
             self.calls.append(c)
@@ -115,7 +119,7 @@ class Workload:
         c = self.calls[i % len(self.calls)]
         if ev is not None:
             ev[0].record()
-        m.refresh_mla_metadata(self.md, self.seqlens, self.indices)
+        m.refresh_mla_metadata(self.mds[i % len(self.calls)], self.seqlens, self.indices)
         if ev is not None:
             ev[1].record()
         c.partial()
@@ -126,7 +130,10 @@ class Workload:
             ev[3].record()
 
     def capture(self):
-        """One HIP graph per pool copy holding the whole step."""
+        """HIP graphs holding consecutive whole steps, one step per pool copy
+        in rotation: graphs[n] runs steps on copies 0 .. n - 1, so a full
+        rotation is one graph launch (as a serving loop launches one graph
+        per decode step of many kernels, not one per kernel)."""
         import torch
         import mla_paged_kv_metadata_amd as m
         side = torch.cuda.Stream()
@@ -136,39 +143,47 @@ class Workload:
                 self.step(i)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        self.graphs = []
-        for c in self.calls:
+        self.graphs = {}
+        for n in range(1, len(self.calls) + 1):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                m.refresh_mla_metadata(self.md, self.seqlens, self.indices)
-                c.partial()
-                c.combine()
-            self.graphs.append(g)
+                for r, c in enumerate(self.calls[:n]):
+                    m.refresh_mla_metadata(self.mds[r], self.seqlens, self.indices)
+                    c.partial()
+                    c.combine()
+            self.graphs[n] = g
         torch.cuda.synchronize()
 
     def check_graph(self):
-        """Each graph's out/lse must equal the eager step's, bit for bit."""
+        """Each graph's out/lse must equal the eager step's, bit for bit (all
+        pool copies hold the same logical cache, so every step of a graph
+        writes the same result)."""
         import torch
         c0 = self.calls[0]
-        for r, g in enumerate(self.graphs):
-            self.step(r)
-            torch.cuda.synchronize()
-            ref_o, ref_l = c0.out.clone(), c0.lse.clone()
+        self.step(0)
+        torch.cuda.synchronize()
+        ref_o, ref_l = c0.out.clone(), c0.lse.clone()
+        for n, g in self.graphs.items():
             c0.out.fill_(0)
             c0.lse.fill_(0)
             g.replay()
             torch.cuda.synchronize()
             if not (torch.equal(c0.out, ref_o) and torch.equal(c0.lse, ref_l)):
-                raise RuntimeError(f"graph replay {r} differs from the eager step")
+                raise RuntimeError(f"graph of {n} steps differs from the eager step")
+
+    def _replay_steps(self, steps: int):
+        full = len(self.calls)
+        for _ in range(steps // full):
+            self.graphs[full].replay()
+        if steps % full:
+            self.graphs[steps % full].replay()
 
     def time_graph(self, steps: int, warmup: int) -> float:
         import torch
-        for i in range(warmup):
-            self.graphs[i % len(self.graphs)].replay()
+        self._replay_steps(warmup)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            self.graphs[i % len(self.graphs)].replay()
+        self._replay_steps(steps)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
@@ -387,7 +402,7 @@ def main():
             "sum_seqlens": int(prim.inp.seqlens.sum()),
             "kv_bytes": kv, "kv_format": "bf16", "page_size": 64,
             "num_parts": prim.md.num_parts, "pool_replicas": args.replicas,
-            "step": "HIP graph replay of metadata + split-KV + combine",
+            "step": "metadata + split-KV + combine, replayed from HIP graphs of 3 consecutive steps",
         },
         "timing_ms": {k: round(v, 5) for k, v in tm.items()},
         "roofline": {

@@ -223,7 +223,9 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
 __global__ __launch_bounds__(64) void metadata_wave_kernel(const int32_t* __restrict__ seqlens, int units,
                                                           int num_parts, int32_t* __restrict__ md,
                                                           int32_t* __restrict__ num_splits) {
-  __shared__ int32_t rows[kMaxParts * kPartRow];
+  // num_parts rows of LDS (dynamic: small enough to share a CU with a
+  // decode workgroup when schedules are built alongside a decode).
+  extern __shared__ int32_t rows[];
   const int lane = threadIdx.x;
   const int P = num_parts;
   const long long c0 = kUnitOverhead;
@@ -286,8 +288,8 @@ hipError_t launch_metadata(const int32_t* seqlens, const int32_t* indices, int s
                            hipStream_t stream) {
   if (num_parts < 1 || num_parts > kMaxParts) return hipErrorInvalidValue;
   if (indices == nullptr && units <= 64) {
-    hipLaunchKernelGGL(metadata_wave_kernel, dim3(1), dim3(64), 0, stream, seqlens, units, num_parts, md,
-                       num_splits);
+    hipLaunchKernelGGL(metadata_wave_kernel, dim3(1), dim3(64), (size_t)num_parts * kPartRow * sizeof(int32_t),
+                       stream, seqlens, units, num_parts, md, num_splits);
   } else if (indices == nullptr) {
     hipLaunchKernelGGL(metadata_kernel<false>, dim3(1), dim3(kMdThreads), 0, stream, seqlens, indices,
                        s_q, topk, 0, units, num_parts, md, num_splits);
