@@ -167,6 +167,29 @@ int mla_decode_kvcache(const mla_decode_args *args, void *stream);
 int mla_decode_partial(const mla_decode_args *args, void *stream);
 int mla_decode_combine(const mla_decode_args *args, void *stream);
 
+/*
+ * Debug audit of the values a decode call reads from device memory, which
+ * the kernels take on trust for speed (sao.pub FlashMLA overview, 三、动手实践,
+ * pitfall 3: the sparse kernel does no input checking, so a malformed
+ * `indices` gives silently wrong results).  SYNCHRONOUS and slow: it copies
+ * cache_seqlens, block_table, indices, tile_metadata and num_splits to host
+ * memory on `stream`, waits for the stream, and checks there that
+ *   - every check of mla_decode_kvcache passes (shapes, pointers, workspace);
+ *   - num_pages >= 1 and every L_b >= 0 with ceil(L_b / 64) blocks fitting
+ *     in max_blocks_per_seq;
+ *   - block_table holds a page in [0, num_pages) for every block a visible
+ *     key lies in (dense: all blocks of the sequence; sparse: the blocks of
+ *     the unmasked indices);
+ *   - tile_metadata and num_splits are the schedule mla_get_metadata builds
+ *     for these cache_seqlens / indices and num_parts (not stale): header,
+ *     blocks per unit, parts covering every (unit, block) once in order,
+ *     split indices and split counts.
+ * Launches nothing and writes no device memory.  Returns MLA_OK, or
+ * MLA_ERR_INVALID_ARGUMENT with mla_last_error() naming the first problem
+ * (MLA_ERR_HIP if a copy or the wait fails).  Not capturable in a graph.
+ */
+int mla_validate_inputs(const mla_decode_args *args, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *mla_last_error(void);
 

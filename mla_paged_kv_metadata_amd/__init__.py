@@ -16,5 +16,6 @@ from .api import (  # noqa: F401
     default_softmax_scale,
     refresh_mla_metadata,
     DecodeCall,
+    validate_inputs,
 )
 from ._lib import MlaError, LIB_PATH, load as load_library  # noqa: F401

@@ -227,3 +227,17 @@ class DecodeCall:
 
     def combine(self):
         self._call(self._lib.mla_decode_combine)
+
+    def validate(self):
+        """Synchronous debug audit of the device-resident inputs (block
+        table pages, lengths, indices and the schedule); raises MlaError
+        naming the first problem."""
+        self._call(self._lib.mla_validate_inputs)
+
+
+def validate_inputs(q, kcache, block_table, cache_seqlens, metadata: MlaMetadata,
+                    causal=False, indices=None) -> None:
+    """Debug check of a decode call's inputs before running it (synchronous;
+    allocates the call's outputs and workspace).  Raises MlaError."""
+    DecodeCall(q, kcache, block_table, cache_seqlens, metadata, causal=causal,
+               indices=indices).validate()

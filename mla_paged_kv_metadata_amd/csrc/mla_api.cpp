@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "mla.h"
 #include "mla_device.h"
@@ -188,17 +189,26 @@ MLA_EXPORT int mla_workspace_size(const mla_decode_args* args, size_t* bytes) {
 
 namespace {
 
+// Workspace present and large enough; *o_bytes = offset of the partial lse.
+int check_workspace(const mla_decode_args* a, size_t* o_bytes) {
+  size_t need;
+  workspace_layout(units_of(a->batch, a->s_q, a->topk), a->num_parts,
+                   rows_per_unit(a->s_q, a->h_q, a->topk), o_bytes, &need);
+  if (a->workspace_bytes < need || (!a->workspace && need > 0))
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu needed",
+                a->workspace_bytes, need);
+  return MLA_OK;
+}
+
 int decode_impl(const mla_decode_args* a, void* stream, int which) {
   int st = check_decode_args(a);
   if (st != MLA_OK) return st;
   if (a->batch == 0) return ok();
   const int units = units_of(a->batch, a->s_q, a->topk);
   const int R = rows_per_unit(a->s_q, a->h_q, a->topk);
-  size_t ob, need;
-  workspace_layout(units, a->num_parts, R, &ob, &need);
-  if (a->workspace_bytes < need || (!a->workspace && need > 0))
-    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu needed",
-                a->workspace_bytes, need);
+  size_t ob;
+  st = check_workspace(a, &ob);
+  if (st != MLA_OK) return st;
   mla::DecodeParams p;
   p.q = (const uint8_t*)a->q;
   p.kcache = (const uint8_t*)a->kcache;
@@ -241,4 +251,164 @@ MLA_EXPORT int mla_decode_partial(const mla_decode_args* a, void* stream) {
 
 MLA_EXPORT int mla_decode_combine(const mla_decode_args* a, void* stream) {
   return decode_impl(a, stream, 2);
+}
+
+namespace {
+
+template <typename T>
+int copy_to_host(std::vector<T>* dst, const void* src, size_t n, hipStream_t s, const char* what) {
+  dst->resize(n);
+  if (n == 0) return MLA_OK;
+  const hipError_t e = hipMemcpyAsync(dst->data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "copying %s to the host: %s", what, hipGetErrorString(e));
+  return MLA_OK;
+}
+
+// Keys of query token s of a sequence of length L that any row may see.
+int window_of(const mla_decode_args* a, int L, int s) {
+  if (!a->causal) return L;
+  const int w = L - a->s_q + 1 + s;
+  return w < 0 ? 0 : (w > L ? L : w);
+}
+
+}  // namespace
+
+// Host-side audit of the device-resident values the kernels trust.  Every
+// buffer is copied to the host once; the checks below run there.
+MLA_EXPORT int mla_validate_inputs(const mla_decode_args* a, void* stream) {
+  int st = check_decode_args(a);
+  if (st != MLA_OK) return st;
+  if (a->batch == 0) return ok();
+  size_t ob;
+  st = check_workspace(a, &ob);
+  if (st != MLA_OK) return st;
+  if (a->num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  const bool sparse = a->topk > 0;
+  const int B = a->batch, U = units_of(a->batch, a->s_q, a->topk), P = a->num_parts;
+  const size_t mb = (size_t)a->max_blocks_per_seq;
+  hipStream_t s = (hipStream_t)stream;
+  auto sync = [&]() {
+    const hipError_t e = hipStreamSynchronize(s);
+    return e == hipSuccess ? MLA_OK : fail(MLA_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  };
+  // The schedule's header first: a schedule built for another part or unit
+  // count has another size, so nothing past the header is read before the
+  // counts are known to match.
+  std::vector<int32_t> L, bt, idx, md, ns;
+  if ((st = copy_to_host(&md, a->tile_metadata, mla::kHeader, s, "tile_metadata")) != MLA_OK ||
+      (st = sync()) != MLA_OK)
+    return st;
+  if (md[5] != 0x4D4C4131)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "tile_metadata was not written by mla_get_metadata");
+  if (md[0] != P || md[3] != U)
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "tile_metadata is for %d parts and %d units, the call has %d and %d", md[0], md[3],
+                P, U);
+  if ((st = copy_to_host(&L, a->cache_seqlens, B, s, "cache_seqlens")) != MLA_OK ||
+      (st = copy_to_host(&bt, a->block_table, B * mb, s, "block_table")) != MLA_OK ||
+      (st = copy_to_host(&idx, a->indices, sparse ? (size_t)U * a->topk : 0, s, "indices")) != MLA_OK ||
+      (st = copy_to_host(&md, a->tile_metadata, md_elems(U, P), s, "tile_metadata")) != MLA_OK ||
+      (st = copy_to_host(&ns, a->num_splits, (size_t)U + 1, s, "num_splits")) != MLA_OK ||
+      (st = sync()) != MLA_OK)
+    return st;
+
+  // Sequence lengths, and the pool page of every block a visible key lies in.
+  for (int b = 0; b < B; ++b) {
+    if (L[b] < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seqlens[%d] = %d is negative", b, L[b]);
+    const long long nb = ((long long)L[b] + mla::kPage - 1) / mla::kPage;
+    if (nb > (long long)mb)
+      return fail(MLA_ERR_INVALID_ARGUMENT,
+                  "cache_seqlens[%d] = %d needs %lld blocks, more than max_blocks_per_seq %zu", b,
+                  L[b], nb, mb);
+    auto bad_page = [&](long long j) {
+      const int32_t pg = bt[b * mb + j];
+      return fail(MLA_ERR_INVALID_ARGUMENT,
+                  "block_table[%d][%lld] = %d is outside the pool [0, %d)", b, j, pg, a->num_pages);
+    };
+    if (!sparse) {
+      for (long long j = 0; j < nb; ++j) {
+        const int32_t pg = bt[b * mb + j];
+        if (pg < 0 || pg >= a->num_pages) return bad_page(j);
+      }
+      continue;
+    }
+    for (int q = 0; q < a->s_q; ++q) {
+      const int W = window_of(a, L[b], q);
+      const int32_t* row = &idx[((size_t)b * a->s_q + q) * a->topk];
+      for (int i = 0; i < a->topk; ++i) {
+        if (row[i] < 0 || row[i] >= W) continue;   // masked: no page is read for it
+        const int32_t pg = bt[b * mb + (row[i] >> 6)];
+        if (pg < 0 || pg >= a->num_pages) return bad_page(row[i] >> 6);
+      }
+    }
+  }
+
+  // The schedule must be the one mla_get_metadata builds for these lengths
+  // (and indices): header, blocks per unit, and parts that cover every
+  // (unit, block) once, in order, with split indices counted by num_splits.
+  const int32_t* hdr = md.data();
+  const int32_t* nblk = md.data() + mla::kHeader + (size_t)mla::kPartRow * P;
+  long long total = 0;
+  for (int u = 0; u < U; ++u) {
+    int want;
+    if (!sparse) {
+      want = (L[u] + mla::kPage - 1) / mla::kPage;
+    } else {
+      // Blocks up to the last entry that indexes the sequence.
+      const int Lb = L[u / a->s_q];
+      const int32_t* row = &idx[(size_t)u * a->topk];
+      int end = 0;
+      for (int i = 0; i < a->topk; ++i)
+        if (row[i] >= 0 && row[i] < Lb) end = i + 1;
+      want = (end + mla::kPage - 1) / mla::kPage;
+    }
+    if (want < 1) want = 1;
+    if (nblk[u] != want)
+      return fail(MLA_ERR_INVALID_ARGUMENT,
+                  "tile_metadata is stale: unit %d spans %d blocks there, %d for these inputs", u,
+                  nblk[u], want);
+    total += want;
+  }
+  if (hdr[4] != total)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "tile_metadata total blocks %d, expected %lld", hdr[4], total);
+  if (ns[0] != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits[0] = %d, expected 0", ns[0]);
+  int cu = 0, cj = 0;   // next (unit, block) to be covered
+  int last_u = -1, next_split = 0;
+  for (int p = 0; p < P; ++p) {
+    const int32_t* r = md.data() + mla::kHeader + (size_t)mla::kPartRow * p;
+    if (r[0] < 0) continue;
+    const int u0 = r[0], j0 = r[1], u1 = r[2], j1 = r[3];
+    if (u0 != cu || j0 != cj || u1 < u0 || u1 >= U || j1 < 1 || j1 > nblk[u1] ||
+        (u1 == u0 && j1 <= j0))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "tile_metadata part %d {%d, %d, %d, %d} does not continue "
+                  "the schedule at unit %d block %d", p, u0, j0, u1, j1, cu, cj);
+    if (r[5] != L[sparse ? u0 / a->s_q : u0] || r[6] != nblk[u0])
+      return fail(MLA_ERR_INVALID_ARGUMENT, "tile_metadata part %d has a stale length or block count", p);
+    // Split index of u0 in this part: one past the previous part's if that
+    // one also held u0, else 0.
+    const int split = (u0 == last_u) ? next_split : 0;
+    if (r[4] != split)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "tile_metadata part %d: split index %d, expected %d", p,
+                  r[4], split);
+    for (int u = u0; u <= u1; ++u) {
+      const int k = (u == u0) ? split + 1 : 1;   // splits of u seen so far
+      const bool ends = (u < u1) || (j1 == nblk[u1]);
+      if (ends && ns[u + 1] - ns[u] != k)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "num_splits: unit %d has %d splits, the parts give %d", u,
+                    ns[u + 1] - ns[u], k);
+    }
+    last_u = u1;
+    next_split = (u1 == u0) ? split + 1 : 1;
+    if (j1 == nblk[u1]) {
+      cu = u1 + 1;
+      cj = 0;
+    } else {
+      cu = u1;
+      cj = j1;
+    }
+  }
+  if (cu != U)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "tile_metadata parts stop at unit %d block %d of %d units", cu,
+                cj, U);
+  return ok();
 }

@@ -94,6 +94,9 @@ def test_decode_rejects_bad_arguments_without_launching(lib, field, value, code)
     a = _args(**{field: value})
     assert lib.mla_decode_kvcache(ctypes.byref(a), None) == code
     assert lib.mla_last_error() != b""
+    # the debug audit applies the same checks before it reads any buffer
+    assert lib.mla_validate_inputs(ctypes.byref(a), None) == code
+    assert lib.mla_last_error() != b""
 
 
 def test_decode_rejects_null_pointers_and_small_workspace(lib):
@@ -116,3 +119,15 @@ def test_get_metadata_rejects_bad_arguments(lib):
 def test_empty_batch_decode_is_a_no_op(lib):
     a = _args(batch=0)
     assert lib.mla_decode_kvcache(ctypes.byref(a), None) == 0
+    assert lib.mla_validate_inputs(ctypes.byref(a), None) == 0
+
+
+def test_validate_checks_pointers_and_workspace_before_reading(lib):
+    assert lib.mla_validate_inputs(None, None) == -1
+    a = _args()
+    assert lib.mla_validate_inputs(ctypes.byref(a), None) == -1   # q etc. are NULL
+    fake = 0x1000   # never dereferenced: the workspace check fails first
+    a = _args(q=fake, kcache=fake, block_table=fake, cache_seqlens=fake, tile_metadata=fake,
+              num_splits=fake, out=fake, lse=fake, workspace=fake, workspace_bytes=16)
+    assert lib.mla_validate_inputs(ctypes.byref(a), None) == -3
+    assert b"workspace" in lib.mla_last_error()
