@@ -61,22 +61,21 @@ __device__ __forceinline__ long long wg_exclusive_scan(long long v, long long* s
   return before + incl - v;
 }
 
-// Blocks of 64 keys that sparse unit u spans.  One wave; the index row is
+// Largest entry position in [lo, hi) of index row idx whose value lies in
+// [0, L), or -1 (wave-wide; lo, hi multiples of 4 when vec4).  The row is
 // read in batches of eight loads per lane, all issued before any is used.
-__device__ __forceinline__ int sparse_unit_blocks(const int32_t* __restrict__ indices, int topk, int L,
-                                                  int u, bool vec4, int lane) {
+__device__ __forceinline__ int last_valid_in(const int32_t* __restrict__ idx, int lo, int hi, int L, bool vec4,
+                                             int lane) {
   constexpr int kBatch = 8;
-  const int32_t* idx = indices + (size_t)u * topk;
   int last = -1;
   if (vec4) {
     const int4* idx4 = (const int4*)idx;
-    const int n4 = topk / 4;
-    for (int base = 0; base < n4; base += 64 * kBatch) {
+    for (int base = lo / 4; base < hi / 4; base += 64 * kBatch) {
       int4 t[kBatch];
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
         const int e4 = base + lane + 64 * k;
-        t[k] = e4 < n4 ? idx4[e4] : make_int4(-1, -1, -1, -1);
+        t[k] = e4 < hi / 4 ? idx4[e4] : make_int4(-1, -1, -1, -1);
       }
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
@@ -88,12 +87,12 @@ __device__ __forceinline__ int sparse_unit_blocks(const int32_t* __restrict__ in
       }
     }
   } else {
-    for (int base = 0; base < topk; base += 64 * kBatch) {
+    for (int base = lo; base < hi; base += 64 * kBatch) {
       int t[kBatch];
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
         const int e = base + lane + 64 * k;
-        t[k] = e < topk ? idx[e] : -1;
+        t[k] = e < hi ? idx[e] : -1;
       }
 #pragma unroll
       for (int k = 0; k < kBatch; ++k)
@@ -102,8 +101,63 @@ __device__ __forceinline__ int sparse_unit_blocks(const int32_t* __restrict__ in
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) last = max(last, __shfl_xor(last, m));
-  const int n = (last + 1 + kPage - 1) / kPage;
-  return n < 1 ? 1 : n;
+  return last;
+}
+
+// The last kTail entries of an index row, one 16-byte load per lane (vec4)
+// or four 4-byte loads per lane, issued without waiting for them.
+constexpr int kTail = 256;
+struct Tail {
+  int4 t;
+};
+__device__ __forceinline__ Tail load_tail(const int32_t* __restrict__ idx, int topk, bool vec4, int lane) {
+  Tail r;
+  const int lo = topk > kTail ? topk - kTail : 0;
+  if (vec4) {
+    const int e4 = lo / 4 + lane;
+    r.t = e4 < topk / 4 ? ((const int4*)idx)[e4] : make_int4(-1, -1, -1, -1);
+  } else {
+    const int e = lo + 4 * lane;
+    r.t.x = e < topk ? idx[e] : -1;
+    r.t.y = e + 1 < topk ? idx[e + 1] : -1;
+    r.t.z = e + 2 < topk ? idx[e + 2] : -1;
+    r.t.w = e + 3 < topk ? idx[e + 3] : -1;
+  }
+  return r;
+}
+// Largest valid entry position in the tail (wave-wide), or -1.
+__device__ __forceinline__ int tail_last(const Tail& r, int topk, int L, int lane) {
+  const int e = (topk > kTail ? topk - kTail : 0) + 4 * lane;
+  int last = -1;
+  if (r.t.x >= 0 && r.t.x < L) last = e;
+  if (r.t.y >= 0 && r.t.y < L) last = e + 1;
+  if (r.t.z >= 0 && r.t.z < L) last = e + 2;
+  if (r.t.w >= 0 && r.t.w < L) last = e + 3;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) last = max(last, __shfl_xor(last, m));
+  return last;
+}
+
+// Blocks of 64 keys that sparse units ua and ub (ub < 0: none) span, up to
+// each one's last entry pointing into its sequence.  One wave; the rows are
+// read from the end: the last 256 entries of both rows first, the rest of a
+// row only when none of those is valid.
+__device__ __forceinline__ void sparse_unit_blocks(const int32_t* __restrict__ indices,
+                                                   const int32_t* __restrict__ seqlens, int s_q, int topk,
+                                                   int ua, int ub, bool vec4, int lane, int* na, int* nb) {
+  const int32_t* ia = indices + (size_t)ua * topk;
+  const int32_t* ib = indices + (size_t)(ub >= 0 ? ub : ua) * topk;
+  const int La = seqlens[ua / s_q];
+  const int Lb = ub >= 0 ? seqlens[ub / s_q] : 0;
+  const Tail ta = load_tail(ia, topk, vec4, lane);
+  const Tail tb = load_tail(ib, topk, vec4, lane);
+  int la = tail_last(ta, topk, La, lane);
+  int lb = ub >= 0 ? tail_last(tb, topk, Lb, lane) : -1;
+  const int rest = topk > kTail ? topk - kTail : 0;
+  if (la < 0 && rest > 0) la = last_valid_in(ia, 0, rest, La, vec4, lane);
+  if (ub >= 0 && lb < 0 && rest > 0) lb = last_valid_in(ib, 0, rest, Lb, vec4, lane);
+  *na = max(1, (la + 1 + kPage - 1) / kPage);
+  *nb = max(1, (lb + 1 + kPage - 1) / kPage);
 }
 
 __device__ __forceinline__ int dense_unit_blocks(int L) {
@@ -135,11 +189,18 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
   // Block counts and the total cost.
   long long cost = 0;
   if (SPARSE) {
-    for (int u = wave; u < units; u += kMdWaves) {
-      const int n = sparse_unit_blocks(indices, topk, seqlens[u / s_q], u, vec4 != 0, lane);
+    // Wave w takes units w and w + 16, then w + 32 and w + 48, ...
+    for (int u = wave; u < units; u += 2 * kMdWaves) {
+      const int u2 = u + kMdWaves < units ? u + kMdWaves : -1;
+      int n, n2;
+      sparse_unit_blocks(indices, seqlens, s_q, topk, u, u2, vec4 != 0, lane, &n, &n2);
       if (lane == 0) {
         unit_blocks[u] = n;
         cost += n + c0;
+        if (u2 >= 0) {
+          unit_blocks[u2] = n2;
+          cost += n2 + c0;
+        }
       }
     }
     // The counts are read back by other waves of this workgroup after the

@@ -101,6 +101,41 @@ def test_schedule_matches_oracle_bitwise():
         S.check_schedule(ref_md, ref_ns, nb)
 
 
+@pytest.mark.parametrize("topk", [2048, 1001, 200])
+def test_sparse_schedule_finds_last_valid_entry_anywhere(topk):
+    """Block counts of sparse units whose last valid entry lies in the last
+    256 entries of the row, just before them, at the very start, or nowhere,
+    for 16-byte-multiple rows, other rows and rows shorter than 256."""
+    from oracle import splitkv_schedule as S
+    import torch as T
+    from mla_paged_kv_metadata_amd import get_mla_metadata
+    rng = np.random.default_rng(91 + topk)
+    ends = [topk - 1, topk - 256, topk - 257, topk // 2, 1, 0, -1]   # last valid position (-1: none)
+    ends = [e for e in ends if e < topk]
+    b, s_q = len(ends), 2
+    sl = rng.integers(3000, 9000, size=b).astype(np.int32)
+    ind = np.full((b, s_q, topk), -1, dtype=np.int32)
+    for i, e in enumerate(ends):
+        L = int(sl[i])
+        for s in range(s_q):
+            row = rng.integers(0, L, size=topk).astype(np.int32)
+            # past the last valid position: masked entries, -1 or >= L
+            tail = np.arange(topk) > e
+            row[tail] = np.where(rng.random(int(tail.sum())) < 0.5, -1, L + rng.integers(0, 50, int(tail.sum())))
+            ind[i, s] = row
+    log(f"sparse schedule topk={topk} ends={ends}")
+    nb = S.unit_blocks_sparse(sl, ind)
+    want = [max(1, (e + 1 + 63) // 64) for e in ends]
+    assert list(nb[::s_q]) == want   # the oracle's own count, by construction
+    for P in (8, 40):
+        md = get_mla_metadata(T.from_numpy(sl).cuda(), s_q * 16, 1, s_q=s_q, indices=T.from_numpy(ind).cuda(),
+                              num_parts=P)
+        T.cuda.synchronize()
+        ref_md, ref_ns = S.schedule(nb, P, 2, unit_len=np.repeat(sl, s_q))
+        assert np.array_equal(md.tile_metadata.cpu().numpy(), ref_md), P
+        assert np.array_equal(md.num_splits.cpu().numpy(), ref_ns), P
+
+
 def test_single_key_returns_v_row_bitwise():
     cfg = gen.small_config(3, 1, 16, [1, 1, 1], seed=41)
     inp = gen.make_inputs(cfg, poison=True)
