@@ -42,6 +42,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const float* lrow = ws_lse + (size_t)base * R + r;
   // Lane i keeps lse_i of the first 64 splits.
   const float own = lane < k ? lrow[(size_t)lane * R] : -INFINITY;
+  // The first eight partial rows do not depend on the weights: their loads
+  // go out together with the lse loads.
+  constexpr int kPre = 8;
+  const float* src = ws_o + ((size_t)base * R + r) * kDv + 8 * lane;
+  const size_t stride = (size_t)R * kDv;
+  f32x4 pre[2 * kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    if (j < k) {
+      pre[2 * j] = *(const f32x4*)(src + j * stride);
+      pre[2 * j + 1] = *(const f32x4*)(src + j * stride + 4);
+    } else {
+      pre[2 * j] = pre[2 * j + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   float M = own;
   for (int i = 64 + lane; i < k; i += 64) M = fmaxf(M, lrow[(size_t)i * R]);
   M = wave_max(M);
@@ -56,10 +71,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   S = wave_sum(S);
   const float lse_r = M + fast_log2(S) * kLn2;
   const float w_own = fast_exp2((own - lse_r) * kLog2e);
-  const float* src = ws_o + ((size_t)base * R + r) * kDv + 8 * lane;
-  const size_t stride = (size_t)R * kDv;
   f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
-  int i = 0;
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const float w = j < k ? __shfl(w_own, j) : 0.f;
+    a0 += w * pre[2 * j];
+    a1 += w * pre[2 * j + 1];
+  }
+  int i = kPre;
   for (; i + 4 <= k; i += 4) {
     f32x4 x[8];
 #pragma unroll
