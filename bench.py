@@ -351,7 +351,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--replicas", type=int, default=6)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true",
@@ -411,7 +411,7 @@ def main():
             "sum_seqlens": int(prim.inp.seqlens.sum()),
             "kv_bytes": kv, "kv_format": "bf16", "page_size": 64,
             "num_parts": prim.md.num_parts, "pool_replicas": args.replicas,
-            "step": "metadata + split-KV + combine, replayed from HIP graphs of 3 consecutive steps",
+            "step": f"metadata + split-KV + combine, replayed from HIP graphs of {args.replicas} consecutive steps",
         },
         "timing_ms": {k: round(v, 5) for k, v in tm.items()},
         # KV bytes over the decode kernels alone (split-KV + combine, HIP
