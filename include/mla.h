@@ -137,7 +137,8 @@ int mla_get_metadata(const int32_t *cache_seqlens, const int32_t *indices, int b
                      int32_t *tile_metadata, int32_t *num_splits, void *stream);
 
 /* Bytes of device workspace mla_decode_kvcache needs for these arguments
- * (fp32 partial outputs and partial log-sum-exps of split sequences). */
+ * (bf16 partial outputs, each normalised by its own row sum, and fp32
+ * partial log-sum-exps of split sequences). */
 int mla_workspace_size(const mla_decode_args *args, size_t *bytes);
 
 /*

@@ -74,11 +74,12 @@ size_t md_elems(int units, int parts) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: partial O [slots, R, 512] fp32 then partial lse [slots, R].
-// Every part boundary splits at most one unit, so slots <= units + parts.
+// Workspace: partial O [slots, R, 512] bf16 then partial lse [slots, R]
+// fp32.  Every part boundary splits at most one unit, so slots <= units +
+// parts.
 void workspace_layout(int units, int parts, int R, size_t* o_bytes, size_t* total) {
   const size_t slots = (size_t)units + (size_t)parts;
-  *o_bytes = align_up(slots * (size_t)R * mla::kDv * sizeof(float), 256);
+  *o_bytes = align_up(slots * (size_t)R * mla::kDv * sizeof(uint16_t), 256);
   *total = *o_bytes + align_up(slots * (size_t)R * sizeof(float), 256);
 }
 
@@ -219,7 +220,7 @@ int decode_impl(const mla_decode_args* a, void* stream, int which) {
   p.num_splits = a->num_splits;
   p.out = (uint16_t*)a->out;
   p.lse = a->lse;
-  p.ws_o = (float*)a->workspace;
+  p.ws_o = (uint16_t*)a->workspace;
   p.ws_lse = (float*)((uint8_t*)a->workspace + ob);
   p.batch = a->batch;
   p.s_q = a->s_q;

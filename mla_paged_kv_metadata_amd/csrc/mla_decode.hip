@@ -21,14 +21,25 @@ namespace mla {
 // ---------------------------------------------------------------------------
 // Combine: merge the k_u partial results of every split unit.
 //   lse = log sum_i exp(lse_i);  out = sum_i exp(lse_i - lse) * O_i
-// One wave per query row; lanes own 8 output dims each.  The partial lses
-// are loaded by the lanes in parallel (64 at a time) and their weights are
-// formed in-lane; the partial rows are then summed four at a time, so that
-// eight 16-byte loads per lane are in flight instead of one round trip per
-// split.
+// One wave per query row; lanes own 8 output dims each, i.e. one 16-byte
+// load of bf16 partial values per partial row.  The partial lses are loaded
+// by the lanes in parallel (64 at a time), together with the first eight
+// partial rows (which do not depend on the weights); the weights are formed
+// in-lane and further partial rows are summed eight at a time.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void acc_bf16x8(f32x4& a0, f32x4& a1, float w, const u32x4& v) {
+  a0[0] += w * __builtin_bit_cast(float, v[0] << 16);
+  a0[1] += w * __builtin_bit_cast(float, v[0] & 0xFFFF0000u);
+  a0[2] += w * __builtin_bit_cast(float, v[1] << 16);
+  a0[3] += w * __builtin_bit_cast(float, v[1] & 0xFFFF0000u);
+  a1[0] += w * __builtin_bit_cast(float, v[2] << 16);
+  a1[1] += w * __builtin_bit_cast(float, v[2] & 0xFFFF0000u);
+  a1[2] += w * __builtin_bit_cast(float, v[3] << 16);
+  a1[3] += w * __builtin_bit_cast(float, v[3] & 0xFFFF0000u);
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ num_splits,
-                                                      const float* __restrict__ ws_o,
+                                                      const uint16_t* __restrict__ ws_o,
                                                       const float* __restrict__ ws_lse,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse, int R) {
@@ -42,21 +53,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const float* lrow = ws_lse + (size_t)base * R + r;
   // Lane i keeps lse_i of the first 64 splits.
   const float own = lane < k ? lrow[(size_t)lane * R] : -INFINITY;
-  // The first eight partial rows do not depend on the weights: their loads
-  // go out together with the lse loads.
   constexpr int kPre = 8;
-  const float* src = ws_o + ((size_t)base * R + r) * kDv + 8 * lane;
+  const uint16_t* src = ws_o + ((size_t)base * R + r) * kDv + 8 * lane;
   const size_t stride = (size_t)R * kDv;
-  f32x4 pre[2 * kPre];
+  u32x4 pre[kPre];
 #pragma unroll
-  for (int j = 0; j < kPre; ++j) {
-    if (j < k) {
-      pre[2 * j] = *(const f32x4*)(src + j * stride);
-      pre[2 * j + 1] = *(const f32x4*)(src + j * stride + 4);
-    } else {
-      pre[2 * j] = pre[2 * j + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
+  for (int j = 0; j < kPre; ++j) pre[j] = j < k ? *(const u32x4*)(src + j * stride) : u32x4{0, 0, 0, 0};
   float M = own;
   for (int i = 64 + lane; i < k; i += 64) M = fmaxf(M, lrow[(size_t)i * R]);
   M = wave_max(M);
@@ -71,34 +73,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   S = wave_sum(S);
   const float lse_r = M + fast_log2(S) * kLn2;
   const float w_own = fast_exp2((own - lse_r) * kLog2e);
+  auto weight = [&](int s) -> float {
+    return s < 64 ? __shfl(w_own, s) : fast_exp2((lrow[(size_t)s * R] - lse_r) * kLog2e);
+  };
   f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
-  for (int j = 0; j < kPre; ++j) {
-    const float w = j < k ? __shfl(w_own, j) : 0.f;
-    a0 += w * pre[2 * j];
-    a1 += w * pre[2 * j + 1];
-  }
+  for (int j = 0; j < kPre; ++j) acc_bf16x8(a0, a1, j < k ? __shfl(w_own, j) : 0.f, pre[j]);
   int i = kPre;
-  for (; i + 4 <= k; i += 4) {
-    f32x4 x[8];
+  for (; i + 8 <= k; i += 8) {
+    u32x4 x[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = *(const f32x4*)(src + (i + j) * stride);
-      x[2 * j + 1] = *(const f32x4*)(src + (i + j) * stride + 4);
-    }
+    for (int j = 0; j < 8; ++j) x[j] = *(const u32x4*)(src + (i + j) * stride);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = i + j;
-      const float w = s < 64 ? __shfl(w_own, s) : fast_exp2((lrow[(size_t)s * R] - lse_r) * kLog2e);
-      a0 += w * x[2 * j];
-      a1 += w * x[2 * j + 1];
-    }
+    for (int j = 0; j < 8; ++j) acc_bf16x8(a0, a1, weight(i + j), x[j]);
   }
-  for (; i < k; ++i) {
-    const float w = i < 64 ? __shfl(w_own, i) : fast_exp2((lrow[(size_t)i * R] - lse_r) * kLog2e);
-    a0 += w * *(const f32x4*)(src + i * stride);
-    a1 += w * *(const f32x4*)(src + i * stride + 4);
-  }
+  for (; i < k; ++i) acc_bf16x8(a0, a1, weight(i), *(const u32x4*)(src + i * stride));
   u32x4 wv;
   wv[0] = pack_bf16x2(a0[0], a0[1]);
   wv[1] = pack_bf16x2(a0[2], a0[3]);

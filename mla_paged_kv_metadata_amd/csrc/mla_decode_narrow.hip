@@ -360,9 +360,11 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
                                               pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
           if (wave == 0 && gg == 0) p.lse[grow] = lse_nat;
         } else {
-          float* orow = p.ws_o + ((size_t)split * p.R + r) * kDv + dbase;
+          uint16_t* orow = p.ws_o + ((size_t)split * p.R + r) * kDv + dbase;
 #pragma unroll
-          for (int dt = 0; dt < kDimTiles; ++dt) *(f32x4*)(orow + 16 * dt) = o[dt] * inv;
+          for (int dt = 0; dt < kDimTiles; ++dt)
+            *(u32x2*)(orow + 16 * dt) = u32x2{pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
+                                              pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
           if (wave == 0 && gg == 0) p.ws_lse[(size_t)split * p.R + r] = lse_nat;
         }
       }

@@ -359,7 +359,7 @@ __device__ __forceinline__ void load_q(const DecodeParams& p, int u, int row_bas
 }
 
 // Epilogue of one unit: normalise and store O (bf16 out + lse when the unit
-// has one split, else fp32 partials + lse into the split's workspace slot).
+// has one split, else bf16 partials + fp32 lse into the split's workspace slot).
 // Lane holds row l32, dims 256 hf + 32 dt + 8 (r >> 2) + 4 g + (r & 3); both
 // halves hold the same row max, and each its own part of the row sum.
 __device__ __forceinline__ void store_unit(const DecodeParams& p, const f32x16 (&o)[kDimTiles], float m_run,
@@ -386,13 +386,13 @@ __device__ __forceinline__ void store_unit(const DecodeParams& p, const f32x16 (
                                                   pack_bf16x2(o[dt][4 * qd + 2] * inv, o[dt][4 * qd + 3] * inv)};
     if (hf == 0 && g == 0) p.lse[grow] = lse_nat;
   } else {
-    float* orow = p.ws_o + ((size_t)split * p.R + my_row) * kDv + dbase;
+    uint16_t* orow = p.ws_o + ((size_t)split * p.R + my_row) * kDv + dbase;
 #pragma unroll
     for (int dt = 0; dt < kDimTiles; ++dt)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd)
-        *(f32x4*)(orow + 32 * dt + 8 * qd) = f32x4{o[dt][4 * qd] * inv, o[dt][4 * qd + 1] * inv,
-                                                  o[dt][4 * qd + 2] * inv, o[dt][4 * qd + 3] * inv};
+        *(u32x2*)(orow + 32 * dt + 8 * qd) = u32x2{pack_bf16x2(o[dt][4 * qd] * inv, o[dt][4 * qd + 1] * inv),
+                                                  pack_bf16x2(o[dt][4 * qd + 2] * inv, o[dt][4 * qd + 3] * inv)};
     if (hf == 0 && g == 0) p.ws_lse[(size_t)split * p.R + my_row] = lse_nat;
   }
 }

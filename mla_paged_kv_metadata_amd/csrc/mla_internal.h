@@ -18,7 +18,7 @@ struct DecodeParams {
   const int32_t* num_splits;   // [units + 1]
   uint16_t* out;               // bf16 [units*R, 512]
   float* lse;                  // [units*R]
-  float* ws_o;                 // [slots, R, 512]
+  uint16_t* ws_o;              // [slots, R, 512] bf16 partial outputs
   float* ws_lse;               // [slots, R]
   int batch, s_q, h_q;
   int R;                       // query rows per unit

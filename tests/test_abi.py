@@ -80,7 +80,7 @@ def test_workspace_size_is_host_only(lib):
     a = _args()
     assert lib.mla_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
     slots = 2 + 8
-    o = -(-slots * 16 * 512 * 4 // 256) * 256
+    o = -(-slots * 16 * 512 * 2 // 256) * 256   # bf16 partial rows
     l = -(-slots * 16 * 4 // 256) * 256
     assert n.value == o + l
 
