@@ -152,6 +152,13 @@ class Workload:
                     c.partial()
                     c.combine()
             self.graphs[n] = g
+        # The split-KV kernel alone, once per pool copy, back to back: its
+        # launch duration measured without the dispatch latency that HIP
+        # events around a single eager launch include.
+        self.graph_k2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph_k2):
+            for c in self.calls:
+                c.partial()
         torch.cuda.synchronize()
 
     def check_graph(self):
@@ -186,6 +193,21 @@ class Workload:
         self._replay_steps(steps)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
+
+    def time_k2(self, reps: int) -> float:
+        """Mean split-KV launch duration (ms) from HIP events on the launch
+        stream around replays of the graph of back-to-back launches."""
+        import torch
+        for _ in range(2):
+            self.graph_k2.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            self.graph_k2.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(self.calls))
 
     def time(self, steps: int, warmup: int) -> dict:
         import torch
@@ -343,6 +365,8 @@ def run_workload(idx: int, replicas: int, steps: int, warmup: int):
     w.check_graph()
     t = w.time(steps, warmup)
     t["graph_ms_per_step"] = w.time_graph(steps, warmup)
+    t["splitkv_ms_eager_events"] = t["splitkv_ms"]
+    t["splitkv_ms"] = w.time_k2(max(3, steps // len(w.calls)))
     return w, t
 
 
