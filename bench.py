@@ -78,11 +78,11 @@ def algorithmic_bytes(inp) -> dict:
 class Workload:
     """Device-resident inputs (with pool replicas) and prepared calls."""
 
-    def __init__(self, cfg_idx: int, replicas: int):
+    def __init__(self, name: str, replicas: int):
         import torch
         import mla_inputs as gen
         import mla_paged_kv_metadata_amd as m
-        self.cfg = gen.CONFIGS[cfg_idx]
+        self.cfg = gen.WORKLOADS[name]
         t0 = time.time()
         self.inp = gen.make_inputs(self.cfg)
         log(f"[bench] {self.cfg.name}: inputs generated in {time.time() - t0:.1f}s "
@@ -277,45 +277,45 @@ def cpu_baseline(inp, target_s: float) -> dict:
 # The dominant kernel of each workload, as rocprofv3 names it, and the
 # sources it is built from (the counter summary is valid while they match).
 KERNEL_NAMES = {
-    1: "void mla::narrow::narrow_kernel<0, false>(mla::DecodeParams)",
-    2: "mla::wide::offset_kernel(mla::DecodeParams)",
-    3: "void mla::wide::wide_kernel<1, false>(mla::DecodeParams)",
-    4: "void mla::wide::wide_kernel<1, true>(mla::DecodeParams)",
+    "membound": "void mla::narrow::narrow_kernel<0, false>(mla::DecodeParams)",
+    "mtp": "mla::wide::offset_kernel(mla::DecodeParams)",
+    "fp8": "void mla::wide::wide_kernel<1, false>(mla::DecodeParams)",
+    "sparse": "void mla::wide::wide_kernel<1, true>(mla::DecodeParams)",
 }
 KERNEL_SOURCES = {
-    1: ["mla_decode_narrow.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
-    2: ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
-    3: ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
-    4: ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+    "membound": ["mla_decode_narrow.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+    "mtp": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+    "fp8": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+    "sparse": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "narrow_kernel_membound_b64_h16_traffic.md")
 # Kernel trace + MFMA counter summaries of the compute-bound workloads.
 MFMA_FILES = {
-    2: os.path.join(ROOT, "profiles", "offset_kernel_mtp_b128_sq2_h128_kernel_stats.md"),
-    3: os.path.join(ROOT, "profiles", "wide_kernel_fp8_b64_h128_L8192_kernel_stats.md"),
-    4: os.path.join(ROOT, "profiles", "wide_kernel_sparse_b32_h128_top2048_kernel_stats.md"),
+    "mtp": os.path.join(ROOT, "profiles", "offset_kernel_mtp_b128_sq2_h128_kernel_stats.md"),
+    "fp8": os.path.join(ROOT, "profiles", "wide_kernel_fp8_b64_h128_L8192_kernel_stats.md"),
+    "sparse": os.path.join(ROOT, "profiles", "wide_kernel_sparse_b32_h128_top2048_kernel_stats.md"),
 }
 
 
-def sources_sha(cfg_idx: int) -> str:
+def sources_sha(name: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mla_paged_kv_metadata_amd", "csrc")
-    for f in KERNEL_SOURCES[cfg_idx]:
+    for f in KERNEL_SOURCES[name]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg_idx: int):
+def measured_traffic(name: str):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary (a line `traffic-json: {...}`), or None if there is none or it
     was taken on other kernel sources."""
-    if cfg_idx != 1:
+    if name != "membound":
         return None
-    return _summary_json(TRAFFIC_FILE, "traffic-json", cfg_idx)
+    return _summary_json(TRAFFIC_FILE, "traffic-json", name)
 
 
-def _summary_json(path: str, tag: str, cfg_idx: int):
+def _summary_json(path: str, tag: str, name: str):
     """The `tag: {...}` line of a committed counter summary, or None if there
     is none or it was taken on other kernel sources."""
     if not os.path.exists(path):
@@ -324,14 +324,14 @@ def _summary_json(path: str, tag: str, cfg_idx: int):
         for line in fh:
             if line.startswith(tag + ":"):
                 d = json.loads(line.split(":", 1)[1])
-                return d if d.get("sources_sha") == sources_sha(cfg_idx) else None
+                return d if d.get("sources_sha") == sources_sha(name) else None
     return None
 
 
-def measured_mfma(cfg_idx: int):
+def measured_mfma(name: str):
     """MFMA counter figures (MfmaUtil, MFMA flops) of the dominant kernel from
     the committed summary, or None."""
-    return _summary_json(MFMA_FILES[cfg_idx], "mfma-json", cfg_idx) if cfg_idx in MFMA_FILES else None
+    return _summary_json(MFMA_FILES[name], "mfma-json", name) if name in MFMA_FILES else None
 
 
 def pmc_run(which: str):
@@ -340,8 +340,7 @@ def pmc_run(which: str):
     read, 1 GiB written: the counters' calibration), then six eager steps of
     the workload."""
     import torch
-    idx = {"membound": 1, "mtp": 2, "fp8": 3, "sparse": 4}[which]
-    if idx == 1:
+    if which == "membound":
         n = 256 * 1024 * 1024
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -351,16 +350,16 @@ def pmc_run(which: str):
         del src, dst
         torch.cuda.empty_cache()
         log(f"[bench] copy of {n * 4} B x3")
-    w = Workload(idx, 3)
+    w = Workload(which, 3)
     for i in range(6):
         w.step(i)
     torch.cuda.synchronize()
     log(f"[bench] pmc run done: 6 steps of {w.cfg.name} ({w.flops} flops per split-KV launch)")
 
 
-def run_workload(idx: int, replicas: int, steps: int, warmup: int):
+def run_workload(name: str, replicas: int, steps: int, warmup: int):
     import torch
-    w = Workload(idx, replicas)
+    w = Workload(name, replicas)
     w.capture()
     w.check_graph()
     t = w.time(steps, warmup)
@@ -402,19 +401,18 @@ def main():
         return
 
     if args.only is not None:
-        idx = {"mtp": 2, "fp8": 3, "sparse": 4}[args.only]
-        w, t = run_workload(idx, args.replicas, args.steps, args.warmup)
+        w, t = run_workload(args.only, args.replicas, args.steps, args.warmup)
         print(json.dumps({"workload": w.cfg.name, "timing_ms": t,
                           "splitkv_tflops": w.flops / (t["splitkv_ms"] * 1e-3) / 1e12}), flush=True)
         return
 
-    prim, tm = run_workload(1, args.replicas, args.steps, args.warmup)
+    prim, tm = run_workload("membound", args.replicas, args.steps, args.warmup)
     log("[bench] membound timed")
     kv = prim.bytes["kv"]
     step_ms = tm["graph_ms_per_step"]
     value = kv / (step_ms * 1e-3) / 1e9
     achieved = prim.bytes["total"] / (tm["splitkv_ms"] * 1e-3) / 1e9
-    traffic = measured_traffic(1)
+    traffic = measured_traffic("membound")
     result = {
         "metric": "MLA paged decode: KV-read GB/s (h_q=16) and bf16 TFLOPS (h_q=128,s_q=2)",
         "value": round(value, 1),
@@ -442,7 +440,7 @@ def main():
         # events), the schedule being built once per step for all layers.
         "decode_kv_gbs": round(kv / ((tm["splitkv_ms"] + tm["combine_ms"]) * 1e-3) / 1e9, 1),
         "roofline": {
-            "kernel": KERNEL_NAMES[1],
+            "kernel": KERNEL_NAMES["membound"],
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -458,25 +456,25 @@ def main():
                                                 if k in traffic}
     if not args.only_primary:
         extra = {}
-        for idx, key in ((2, "mtp"), (3, "fp8"), (4, "sparse")):
+        for key in ("mtp", "fp8", "sparse"):
             del prim
             torch.cuda.empty_cache()
             log(f"[bench] timing {key}")
-            w, t = run_workload(idx, args.replicas, max(10, args.steps // 2), args.warmup)
+            w, t = run_workload(key, args.replicas, max(10, args.steps // 2), args.warmup)
             step_s = t["graph_ms_per_step"] * 1e-3
             extra[key] = {
                 "workload": w.cfg.name,
                 "ms_per_step": round(t["graph_ms_per_step"], 5),
                 "tflops": round(w.flops / step_s / 1e12, 2),
                 "kv_gbs": round(w.bytes["kv"] / step_s / 1e9, 1),
-                "splitkv_kernel": KERNEL_NAMES[idx],
+                "splitkv_kernel": KERNEL_NAMES[key],
                 "splitkv_ms": round(t["splitkv_ms"], 5),
                 "combine_ms": round(t["combine_ms"], 5),
                 "metadata_ms": round(t["metadata_ms"], 5),
                 "eager_ms_per_step": round(t["wall_ms_per_step"], 5),
                 "splitkv_tflops": round(w.flops / (t["splitkv_ms"] * 1e-3) / 1e12, 2),
                 "mfma_frac_of_bf16_peak": round(w.flops / (t["splitkv_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                "rocprof": measured_mfma(idx),
+                "rocprof": measured_mfma(key),
                 "flops": w.flops,
                 "kv_bytes": w.bytes["kv"],
             }
@@ -486,7 +484,7 @@ def main():
     if not args.no_cpu_baseline:
         import mla_inputs as gen
         log("[bench] cpu baseline (oracle)")
-        inp = gen.make_inputs(gen.CONFIGS[1])
+        inp = gen.make_inputs(gen.WORKLOADS["membound"])
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

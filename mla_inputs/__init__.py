@@ -64,21 +64,21 @@ class Config:
     seed: int = 0
 
 
-# The five workloads the decode is measured and checked on.  Seeds follow the
-# rule seed = 1000 + workload index.
-CONFIGS = [
-    Config("tiny_b2_h16", batch=2, s_q=1, h_q=16, seqlens=[37, 130],
-           seed=1000),
-    Config("membound_b64_h16_varlen", batch=64, s_q=1, h_q=16,
-           seqlens=("uniform", 1, 8192), max_blocks=128, seed=1001),
-    Config("mtp_b128_sq2_h128_causal", batch=128, s_q=2, h_q=128,
-           seqlens=4096, causal=True, seed=1002),
-    Config("fp8_b64_h128_L8192", batch=64, s_q=1, h_q=128, seqlens=8192,
-           fmt=FMT_FP8, seed=1003),
-    Config("sparse_fp8_b32_h128_L32768_top2048", batch=32, s_q=1, h_q=128,
-           seqlens=32768, fmt=FMT_FP8, topk=2048, masked_rows=8,
-           masked_tail=204, seed=1004),
-]
+# The five workloads the decode is measured and checked on, by short name.
+# Seeds: 1000 for tiny, then 1001 .. 1004 in the order listed.
+WORKLOADS = {
+    "tiny": Config("tiny_b2_h16", batch=2, s_q=1, h_q=16, seqlens=[37, 130],
+                   seed=1000),
+    "membound": Config("membound_b64_h16_varlen", batch=64, s_q=1, h_q=16,
+                       seqlens=("uniform", 1, 8192), max_blocks=128, seed=1001),
+    "mtp": Config("mtp_b128_sq2_h128_causal", batch=128, s_q=2, h_q=128,
+                  seqlens=4096, causal=True, seed=1002),
+    "fp8": Config("fp8_b64_h128_L8192", batch=64, s_q=1, h_q=128, seqlens=8192,
+                  fmt=FMT_FP8, seed=1003),
+    "sparse": Config("sparse_fp8_b32_h128_L32768_top2048", batch=32, s_q=1, h_q=128,
+                     seqlens=32768, fmt=FMT_FP8, topk=2048, masked_rows=8,
+                     masked_tail=204, seed=1004),
+}
 
 
 def row_bytes(fmt: int) -> int:

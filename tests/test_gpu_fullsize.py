@@ -33,12 +33,12 @@ def _sample_rows(inp, n, seed):
     return np.array(sorted(pick), dtype=np.int32)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4])
-def test_full_size_sampled_rows(oracle_mod, idx):
-    cfg = gen.CONFIGS[idx]
+@pytest.mark.parametrize("name,seed", [("membound", 901), ("mtp", 902), ("fp8", 903), ("sparse", 904)])
+def test_full_size_sampled_rows(oracle_mod, name, seed):
+    cfg = gen.WORKLOADS[name]
     log(f"full-size {cfg.name}")
     inp = gen.make_inputs(cfg)
     o, l, md = run_gpu(inp)
-    sel = _sample_rows(inp, 96, 900 + idx)
+    sel = _sample_rows(inp, 96, seed)
     ro, rl = oracle_mod.decode(inp, sel=sel)
     compare(o[sel], l[sel], ro, rl, inp.fmt, f"{cfg.name} ({len(sel)} rows, {md.num_parts} parts)")

@@ -25,7 +25,7 @@ def _gpu():
 
 
 def test_tiny_workload(oracle_mod):
-    inp = gen.make_inputs(gen.CONFIGS[0], poison=True)
+    inp = gen.make_inputs(gen.WORKLOADS["tiny"], poison=True)
     o, l, md = run_gpu(inp)
     ro, rl = oracle_mod.decode(inp)
     compare(o, l, ro, rl, inp.fmt, "tiny")

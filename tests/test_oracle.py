@@ -76,7 +76,7 @@ def assert_close_to_brute(oracle_mod, inp, rtol=1e-10, atol=1e-12):
 
 
 def test_tiny_workload_matches_brute_force(oracle_mod):
-    inp = gen.make_inputs(gen.CONFIGS[0], poison=True)
+    inp = gen.make_inputs(gen.WORKLOADS["tiny"], poison=True)
     assert list(inp.seqlens) == [37, 130] and inp.num_pages == 4
     assert sorted(inp.block_table[inp.block_table >= 0].tolist()) == [0, 1, 2, 3]
     assert_close_to_brute(oracle_mod, inp)
