@@ -281,6 +281,19 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
 
 // Dense schedule for at most 64 units: one wave, one unit per lane, the
 // same arithmetic as metadata_kernel without its workgroup scans.
+// Inclusive wave scan of 32-bit values.
+__device__ __forceinline__ uint32_t wave_inclusive_scan32(uint32_t x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Dense schedules of at most 64 units: one wave, one lane per unit.  With
+// n_u <= 2^25 (L_b < 2^31) and at most 64 units every cost position is
+// below 2^32, so the cost line is kept in 32-bit unsigned arithmetic.
 __global__ __launch_bounds__(64) void metadata_wave_kernel(const int32_t* __restrict__ seqlens, int units,
                                                           int num_parts, int32_t* __restrict__ md,
                                                           int32_t* __restrict__ num_splits) {
@@ -289,7 +302,7 @@ __global__ __launch_bounds__(64) void metadata_wave_kernel(const int32_t* __rest
   extern __shared__ int32_t rows[];
   const int lane = threadIdx.x;
   const int P = num_parts;
-  const long long c0 = kUnitOverhead;
+  const uint32_t c0 = kUnitOverhead;
   int32_t* unit_blocks = md + kHeader + kPartRow * P;
   const bool live = lane < units;
   const int Lu = live ? seqlens[lane] : 0;
@@ -297,37 +310,42 @@ __global__ __launch_bounds__(64) void metadata_wave_kernel(const int32_t* __rest
     const int f = i & (kPartRow - 1);
     rows[i] = (f == 0 || f == 2) ? -1 : 0;
   }
-  const long long nb = live ? dense_unit_blocks(Lu) : 0;
+  const uint32_t nb = live ? (uint32_t)dense_unit_blocks(Lu) : 0u;
   if (live) unit_blocks[lane] = (int32_t)nb;
-  const long long c = live ? nb + c0 : 0;
-  const long long incl = wave_inclusive_scan(c, lane);
-  const long long tot_cost = __shfl(incl, 63);
-  const long long T = tot_cost > 0 ? (tot_cost + P - 1) / P : 1;
-  const long long Cu = incl - c;
-  long long f = 0, l = -1;
+  const uint32_t c = live ? nb + c0 : 0u;
+  const uint32_t incl = wave_inclusive_scan32(c, lane);
+  const uint32_t tot_cost = __shfl(incl, 63);
+  const uint32_t T = tot_cost > 0 ? (tot_cost - 1) / (uint32_t)P + 1 : 1u;
+  const uint32_t Cu = incl - c;
+  // Part indices (below 2048) in signed arithmetic, positions unsigned.
+  int f = 0, l = -1;
   if (live) {
-    f = (Cu + c0) / T;
-    l = (Cu + c0 + nb - 1) / T;
+    f = (int)((Cu + c0) / T);
+    l = (int)((Cu + c0 + nb - 1) / T);
   }
-  const long long k = live ? l - f + 1 : 0;
-  const long long kincl = wave_inclusive_scan(k, lane);
+  const uint32_t k = live ? (uint32_t)(l - f + 1) : 0u;
+  const uint32_t kincl = wave_inclusive_scan32(k, lane);
   __syncthreads();   // row defaults before the rows below
   if (live) {
     num_splits[lane + 1] = (int32_t)kincl;
-    const long long lo = lane > 0 ? max(f, (Cu - 1) / T + 1) : f;
-    for (long long pp = lo; pp <= l; ++pp) {
+    // Parts whose first unit is this one: those the previous unit (whose
+    // last block sits at position Cu - 1) does not reach.
+    const int lo = lane > 0 ? max(f, (int)((Cu - 1) / T) + 1) : f;
+    for (int pp = lo; pp <= l; ++pp) {
       int32_t* row = rows + kPartRow * pp;
       row[0] = lane;
-      row[1] = (int32_t)(pp == f ? 0 : pp * T - Cu - c0);
-      row[4] = (int32_t)(pp - f);
+      row[1] = pp == f ? 0 : (int32_t)((uint32_t)pp * T - Cu - c0);
+      row[4] = pp - f;
       row[5] = Lu;
       row[6] = (int32_t)nb;
     }
-    const long long hi = (lane + 1 < units) ? min(l, (Cu + c + c0) / T - 1) : l;
-    for (long long pp = f; pp <= hi; ++pp) {
+    // Parts whose last unit is this one: those the next unit does not
+    // start in.
+    const int hi = (lane + 1 < units) ? min(l, (int)((Cu + c + c0) / T) - 1) : l;
+    for (int pp = f; pp <= hi; ++pp) {
       int32_t* row = rows + kPartRow * pp;
       row[2] = lane;
-      row[3] = (int32_t)(pp == l ? nb : (pp + 1) * T - Cu - c0);
+      row[3] = pp == l ? (int32_t)nb : (int32_t)((uint32_t)(pp + 1) * T - Cu - c0);
     }
   }
   __syncthreads();
@@ -337,11 +355,19 @@ __global__ __launch_bounds__(64) void metadata_wave_kernel(const int32_t* __rest
                       : lane == 1 ? (int32_t)T
                       : lane == 2 ? (int32_t)c0
                       : lane == 3 ? units
-                      : lane == 4 ? (int32_t)(tot_cost - c0 * units)
+                      : lane == 4 ? (int32_t)(tot_cost - c0 * (uint32_t)units)
                       : lane == 5 ? kMagic : 0;
     md[lane] = v;
   }
-  for (int i = lane; i < P * kPartRow; i += 64) md[kHeader + i] = rows[i];
+  // The rows, 16 bytes per lane and store when the buffer allows it.
+  int32_t* dst = md + kHeader;
+  if (((uintptr_t)dst & 15) == 0) {
+    const int4* src4 = (const int4*)rows;
+    int4* dst4 = (int4*)dst;
+    for (int i = lane; i < P * kPartRow / 4; i += 64) dst4[i] = src4[i];
+  } else {
+    for (int i = lane; i < P * kPartRow; i += 64) dst[i] = rows[i];
+  }
 }
 
 hipError_t launch_metadata(const int32_t* seqlens, const int32_t* indices, int s_q, int topk,
