@@ -191,6 +191,31 @@ int mla_decode_combine(const mla_decode_args *args, void *stream);
  */
 int mla_validate_inputs(const mla_decode_args *args, void *stream);
 
+/*
+ * Write new tokens' latent rows into the page pool: the cache update that
+ * precedes a decode step.  Row formats are the decode's (sao.pub FlashMLA
+ * overview, 二、核心功能与架构: 512 FP8 NoPE values, 4 FP32 scales, one per
+ * 128 values, and 64 BF16 RoPE values; 四、进阶玩法: float8_e4m3fn).
+ *
+ *   rows:   [n, 576] bf16 (device, 16-byte aligned, contiguous): the tokens'
+ *           latent rows, RoPE already applied to dims 512..575.
+ *   slots:  [n] int32 (device): token i goes to pool row slots[i] =
+ *           page * 64 + position in page; a slot outside [0, num_pages * 64)
+ *           (e.g. -1) writes nothing.  Two tokens with the same slot: one of
+ *           them is written, which one is unspecified.
+ *   kv_format: MLA_KV_BF16 copies the 1152-byte row.  MLA_KV_FP8_656
+ *           quantises: per group of 128 NoPE values scale = amax / 448 (fp32;
+ *           448 is the largest e4m3fn magnitude), code = x / scale rounded
+ *           to the nearest e4m3fn value, ties to even, after clamping to
+ *           +-448; an all-zero group gets scale 0 and codes 0; the RoPE
+ *           values are copied bit for bit.  NoPE inputs must be finite.
+ *   kcache: the pool (device, 16-byte aligned), num_pages pages in kv_format.
+ * Enqueued on `stream`; n = 0 is a no-op.  The pool rows of other slots are
+ * not touched.
+ */
+int mla_append_kv(const void *rows, const int32_t *slots, int n, int kv_format, void *kcache,
+                  int num_pages, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *mla_last_error(void);
 

@@ -17,5 +17,6 @@ from .api import (  # noqa: F401
     refresh_mla_metadata,
     DecodeCall,
     validate_inputs,
+    append_kv,
 )
 from ._lib import MlaError, LIB_PATH, load as load_library  # noqa: F401

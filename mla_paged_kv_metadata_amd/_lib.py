@@ -29,6 +29,7 @@ EXPORTED = (
     "mla_decode_partial",
     "mla_decode_combine",
     "mla_validate_inputs",
+    "mla_append_kv",
     "mla_last_error",
     "mla_version",
 )
@@ -91,12 +92,13 @@ def load() -> ctypes.CDLL:
     lib.mla_decode_partial.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
     lib.mla_decode_combine.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
     lib.mla_validate_inputs.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
+    lib.mla_append_kv.argtypes = [P, P, i, i, P, i, P]
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
     lib.mla_version.argtypes = []
     for name in ("mla_metadata_size", "mla_metadata_size_for_parts", "mla_get_metadata",
                  "mla_workspace_size", "mla_decode_kvcache", "mla_decode_partial",
-                 "mla_decode_combine", "mla_validate_inputs", "mla_version"):
+                 "mla_decode_combine", "mla_validate_inputs", "mla_append_kv", "mla_version"):
         getattr(lib, name).restype = i
     _lib = lib
     return lib

@@ -241,3 +241,24 @@ def validate_inputs(q, kcache, block_table, cache_seqlens, metadata: MlaMetadata
     allocates the call's outputs and workspace).  Raises MlaError."""
     DecodeCall(q, kcache, block_table, cache_seqlens, metadata, causal=causal,
                indices=indices).validate()
+
+
+def append_kv(rows: torch.Tensor, slots: torch.Tensor, kcache: torch.Tensor) -> torch.Tensor:
+    """Write token i of rows ([n, 576] bf16) into pool row slots[i]
+    (page * 64 + position; outside the pool: skipped) of kcache, as a bf16
+    row or a quantised 656-byte FP8 row depending on kcache's format.
+    Returns kcache."""
+    if rows.dim() != 2 or rows.shape[1] != D_QK or rows.dtype != torch.bfloat16 or not rows.is_contiguous():
+        raise ValueError("rows must be a contiguous bf16 [n, 576] tensor")
+    _need_i32(slots, "slots")
+    if slots.dim() != 1 or slots.shape[0] != rows.shape[0]:
+        raise ValueError("slots must be [n] int32")
+    if kcache.dim() != 4 or kcache.shape[1] != PAGE or not kcache.is_contiguous():
+        raise ValueError("kcache must be a contiguous [num_pages, 64, 1, row] tensor")
+    fmt = _kv_format(kcache)
+    dev = rows.device
+    with torch.cuda.device(dev):
+        _lib.check(_lib.load().mla_append_kv(
+            ctypes.c_void_p(rows.data_ptr()), ctypes.c_void_p(slots.data_ptr()), rows.shape[0], fmt,
+            ctypes.c_void_p(kcache.data_ptr()), kcache.shape[0], ctypes.c_void_p(_stream_ptr(dev))))
+    return kcache

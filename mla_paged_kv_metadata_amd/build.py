@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libmla.so")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["mla_api.cpp", "mla_metadata.hip", "mla_decode.hip", "mla_decode_narrow.hip",
-           "mla_decode_wide.hip"]
+           "mla_decode_wide.hip", "mla_append.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -413,3 +413,20 @@ MLA_EXPORT int mla_validate_inputs(const mla_decode_args* a, void* stream) {
                 cj, U);
   return ok();
 }
+
+MLA_EXPORT int mla_append_kv(const void* rows, const int32_t* slots, int n, int kv_format, void* kcache,
+                             int num_pages, void* stream) {
+  if (n < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n must be >= 0 (got %d)", n);
+  if (kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8_656)
+    return fail(MLA_ERR_UNSUPPORTED, "unknown kv_format %d", kv_format);
+  if (num_pages < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages must be >= 0 (got %d)", num_pages);
+  if (n == 0) return ok();
+  if (!rows || !slots || (!kcache && num_pages > 0))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (((uintptr_t)rows & 15) != 0 || ((uintptr_t)kcache & 15) != 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "rows and kcache must be 16-byte aligned");
+  const hipError_t e = mla::launch_append(rows, slots, n, kv_format, kcache,
+                                          (long long)num_pages * mla::kPage, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}

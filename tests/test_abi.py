@@ -131,3 +131,14 @@ def test_validate_checks_pointers_and_workspace_before_reading(lib):
               num_splits=fake, out=fake, lse=fake, workspace=fake, workspace_bytes=16)
     assert lib.mla_validate_inputs(ctypes.byref(a), None) == -3
     assert b"workspace" in lib.mla_last_error()
+
+
+def test_append_rejects_bad_arguments_without_launching(lib):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: the checks fail first
+    assert lib.mla_append_kv(None, None, 0, 0, None, 0, None) == 0      # nothing to write
+    assert lib.mla_append_kv(fake, fake, -1, 0, fake, 4, None) == -1
+    assert lib.mla_append_kv(fake, fake, 4, 7, fake, 4, None) == -2
+    assert lib.mla_append_kv(fake, fake, 4, 1, fake, -1, None) == -1
+    assert lib.mla_append_kv(None, fake, 4, 1, fake, 4, None) == -1
+    assert lib.mla_append_kv(ctypes.c_void_p(0x1008), fake, 4, 1, fake, 4, None) == -1   # misaligned
+    assert b"aligned" in lib.mla_last_error()
