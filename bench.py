@@ -235,6 +235,48 @@ class Workload:
         }
 
 
+def bench_append(reps: int) -> dict:
+    """mla_append_kv: a bulk append of 65,536 tokens, 64 sequences of 1024
+    tokens each written to consecutive positions of their own pages, the
+    pages scattered over a pool twice that size (FP8 and bf16 rows), and the
+    append of one MTP decode step (128 sequences x 2 tokens at random
+    positions, FP8).  Algorithmic bytes per token: the 1152-byte input row,
+    the 4-byte slot and the written row."""
+    import torch
+    import mla_paged_kv_metadata_amd as m
+    out = {}
+    g = torch.Generator(device="cpu").manual_seed(1005)
+    for label, n, fmt in (("fp8_65536", 65536, 1), ("bf16_65536", 65536, 0), ("fp8_256", 256, 1)):
+        pages = max(2, 2 * n // 64)
+        rows = torch.randn(n, 576, generator=g).to(torch.bfloat16).cuda()
+        if n >= 1024:   # whole pages of consecutive positions, pages scattered
+            page_of = torch.randperm(pages, generator=g)[: n // 64].to(torch.int64)
+            slots = (page_of.repeat_interleave(64) * 64 + torch.arange(64).repeat(n // 64)).to(torch.int32).cuda()
+        else:
+            slots = torch.randperm(pages * 64, generator=g)[:n].to(torch.int32).cuda()
+        if fmt == 1:
+            k = torch.zeros(pages, 64, 1, 656, dtype=torch.uint8, device="cuda")
+        else:
+            k = torch.zeros(pages, 64, 1, 576, dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            m.append_kv(rows, slots, k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            m.append_kv(rows, slots, k)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        row_out = 656 if fmt == 1 else 1152
+        nbytes = n * (1152 + 4 + row_out)
+        out[label] = {"tokens": n, "kv_format": "fp8_656" if fmt == 1 else "bf16", "us": round(ms * 1e3, 2),
+                      "algorithmic_bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del rows, slots, k
+    return out
+
+
 def cpu_baseline(inp, target_s: float) -> dict:
     """The fp64 oracle on a bounded sample of the same workload: whole
     sequences (all their query rows), taken in order until about target_s of
@@ -379,7 +421,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true",
                     help="skip the MTP, FP8 and sparse workloads")
-    ap.add_argument("--only", choices=["mtp", "fp8", "sparse"], default=None,
+    ap.add_argument("--only", choices=["mtp", "fp8", "sparse", "append"], default=None,
                     help="time just this secondary workload (for profiling)")
     ap.add_argument("--pmc-run", nargs="?", const="membound", default=None,
                     choices=["membound", "mtp", "fp8", "sparse"],
@@ -400,6 +442,9 @@ def main():
         pmc_run(args.pmc_run)
         return
 
+    if args.only == "append":
+        print(json.dumps({"append": bench_append(args.steps)}), flush=True)
+        return
     if args.only is not None:
         w, t = run_workload(args.only, args.replicas, args.steps, args.warmup)
         print(json.dumps({"workload": w.cfg.name, "timing_ms": t,
@@ -479,6 +524,8 @@ def main():
                 "kv_bytes": w.bytes["kv"],
             }
             prim = w
+        log("[bench] timing append")
+        extra["append"] = bench_append(max(10, args.steps // 2))
         result["secondary"] = extra
         del prim
     if not args.no_cpu_baseline:

@@ -14,34 +14,15 @@
 //
 // One wave per token, four tokens per 256-thread workgroup.  FP8: lane l
 // holds NoPE values 8 l .. 8 l + 7 (one 16-byte load), the group maximum
-// is reduced over the 16 lanes of its group, and the lane writes its eight
-// codes as one 8-byte store; lanes 0..7 copy the RoPE values.
+// is reduced over the 16 lanes of its group, the quotients are rounded to
+// e4m3fn codes by v_cvt_pk_fp8_f32 (round to nearest even, two per
+// instruction) and the lane writes its eight codes as one 8-byte store;
+// lanes 0..7 copy the RoPE values.
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
 namespace {
-
-// fp32 in [-448, 448] -> e4m3fn code, round to nearest, ties to even.
-// Normal codes (|v| >= 2^-6) keep the top three mantissa bits of the fp32
-// value, rounded at bit 20 with the usual add-and-carry (a carry out of the
-// mantissa raises the exponent, as it should); the exponent is rebiased
-// from 127 to 7.  Below 2^-6 the codes are the multiples of 2^-9: v * 512
-// is exact and rint rounds it to the nearest even integer (8 is the
-// smallest normal, code 0x08).
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t bits = __float_as_uint(v);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const uint32_t a = bits & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x3C800000u) {
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  } else {
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.f);
-  }
-  return sign | code;
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -75,14 +56,35 @@ __global__ __launch_bounds__(256) void append_kernel(const uint8_t* __restrict__
 #pragma unroll
   for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
   const float scale = m / 448.f;
-  uint32_t c[8];
+  // x / scale, correctly rounded, from the correctly rounded reciprocal y:
+  // q0 = x * y is within one ulp of x / scale, the residual x - scale * q0
+  // is exact in an FMA, and q0 + residual * y rounds to the correctly
+  // rounded quotient (Markstein's theorem).  A subnormal scale, whose
+  // reciprocal could overflow, divides directly.
+  const bool normal_scale = scale >= 0x1p-126f;
+  const float y = normal_scale ? 1.f / scale : 0.f;
+  float q[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float q = scale > 0.f ? fminf(fmaxf(x[i] / scale, -448.f), 448.f) : 0.f;
-    c[i] = scale > 0.f ? e4m3_rne(q) : 0u;
+    if (normal_scale) {
+      const float q0 = x[i] * y;
+      // the correction of an exact zero adds +0: the quotient keeps x's sign
+      q[i] = copysignf(fmaf(fmaf(-scale, q0, x[i]), y, q0), x[i]);
+    } else {
+      q[i] = scale > 0.f ? x[i] / scale : 0.f;
+    }
+    q[i] = fminf(fmaxf(q[i], -448.f), 448.f);
   }
-  *(u32x2*)(dst + 8 * lane) = u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                                    c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+  // v_cvt_pk_fp8_f32: two fp32 values to two e4m3fn codes, round to
+  // nearest even (the inputs are already within +-448).
+  u32x2 codes;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * h], q[4 * h + 1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * h + 2], q[4 * h + 3], w, true);
+    codes[h] = scale > 0.f ? (uint32_t)w : 0u;
+  }
+  *(u32x2*)(dst + 8 * lane) = codes;
   if ((lane & 15) == 0) *(float*)(dst + 512 + 4 * (lane >> 4)) = scale;
   if (lane < 8) *(u32x4*)(dst + 528 + 16 * lane) = *(const u32x4*)(src + 1024 + 16 * lane);
 }
