@@ -62,10 +62,12 @@ class Config:
     masked_tail: int = 0       # sparse: how many trailing entries become -1
     max_blocks: Optional[int] = None
     seed: int = 0
+    topk_in_window: bool = False  # sparse + causal: draw each query's indices
+                                  # from the keys it may see
 
 
 # The five workloads the decode is measured and checked on, by short name.
-# Seeds: 1000 for tiny, then 1001 .. 1004 in the order listed.
+# Seeds: 1000 for tiny, then 1001 .. 1005 in the order listed.
 WORKLOADS = {
     "tiny": Config("tiny_b2_h16", batch=2, s_q=1, h_q=16, seqlens=[37, 130],
                    seed=1000),
@@ -78,6 +80,11 @@ WORKLOADS = {
     "sparse": Config("sparse_fp8_b32_h128_L32768_top2048", batch=32, s_q=1, h_q=128,
                      seqlens=32768, fmt=FMT_FP8, topk=2048, masked_rows=8,
                      masked_tail=204, seed=1004),
+    # Sparse prefill: 2048 new tokens at the end of an 8192-token sequence,
+    # each attending to 2048 of the keys its causal window holds.
+    "sparse_prefill": Config("sparse_prefill_fp8_b1_sq2048_h128_L8192_top2048", batch=1, s_q=2048,
+                             h_q=128, seqlens=8192, causal=True, fmt=FMT_FP8, topk=2048,
+                             topk_in_window=True, seed=1005),
 }
 
 
@@ -245,11 +252,14 @@ def make_inputs(cfg: Config, seed: Optional[int] = None, poison: bool = False,
         for b in range(cfg.batch):
             L = int(seqlens[b])
             for s in range(cfg.s_q):
-                if L >= cfg.topk:
-                    indices[b, s] = rng.choice(L, cfg.topk, replace=False).astype(np.int32)
+                W = L
+                if cfg.topk_in_window and cfg.causal:
+                    W = min(max(L - cfg.s_q + 1 + s, 0), L)
+                if W >= cfg.topk:
+                    indices[b, s] = rng.choice(W, cfg.topk, replace=False).astype(np.int32)
                 else:
                     row = np.full(cfg.topk, -1, dtype=np.int32)
-                    row[:L] = rng.permutation(L).astype(np.int32)
+                    row[:W] = rng.permutation(W).astype(np.int32)
                     indices[b, s] = row
         if cfg.masked_rows:
             rows = rng.choice(cfg.batch, cfg.masked_rows, replace=False)
@@ -306,7 +316,7 @@ def permute_pages(inp: Inputs, seed: int) -> Inputs:
 
 
 def small_config(batch, s_q, h_q, seqlens, causal=False, fmt=FMT_BF16, topk=0,
-                 seed=7, max_blocks=None):
+                 seed=7, max_blocks=None, topk_in_window=False):
     return Config(name="custom", batch=batch, s_q=s_q, h_q=h_q,
                   seqlens=list(seqlens), causal=causal, fmt=fmt, topk=topk,
-                  seed=seed, max_blocks=max_blocks)
+                  seed=seed, max_blocks=max_blocks, topk_in_window=topk_in_window)

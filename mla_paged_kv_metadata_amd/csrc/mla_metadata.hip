@@ -175,6 +175,10 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
                                                               int32_t* __restrict__ num_splits) {
   __shared__ long long sh[2][kMdWaves];
   __shared__ int32_t rows[kMaxParts * kPartRow];
+  // Sparse: bit u set when unit u's block count is known from its last
+  // index entry alone (units below kDoneBits).
+  constexpr int kDoneBits = SPARSE ? 65536 : 32;
+  __shared__ uint32_t done[kDoneBits / 32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = num_parts;
   const long long c0 = kUnitOverhead;
@@ -189,17 +193,45 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
   // Block counts and the total cost.
   long long cost = 0;
   if (SPARSE) {
-    // Wave w takes units w and w + 16, then w + 32 and w + 48, ...
-    for (int u = wave; u < units; u += 2 * kMdWaves) {
-      const int u2 = u + kMdWaves < units ? u + kMdWaves : -1;
-      int n, n2;
-      sparse_unit_blocks(indices, seqlens, s_q, topk, u, u2, vec4 != 0, lane, &n, &n2);
-      if (lane == 0) {
-        unit_blocks[u] = n;
-        cost += n + c0;
-        if (u2 >= 0) {
-          unit_blocks[u2] = n2;
-          cost += n2 + c0;
+    for (int i = tid; i < kDoneBits / 32; i += kMdThreads) done[i] = 0u;
+    __syncthreads();
+    // A row whose last entry points into the sequence spans all its blocks
+    // (the usual case): one thread per unit reads just that entry.
+    const int n_all = (topk + kPage - 1) / kPage;
+    for (int u = tid; u < units; u += kMdThreads) {
+      const int last = indices[(size_t)u * topk + topk - 1];
+      if (last >= 0 && last < seqlens[u / s_q]) {
+        unit_blocks[u] = n_all;
+        cost += n_all + c0;
+        if (u < kDoneBits) atomicOr(&done[u >> 5], 1u << (u & 31));
+      }
+    }
+    __syncthreads();
+    // The other rows: wave w looks at units w, w + 16, w + 32, ... (lane l
+    // of a chunk of 1024 units at unit 16 l + w, so that neighbouring open
+    // rows go to different waves) and scans the open rows two at a time
+    // from the end.
+    for (int base = 0; base < units; base += 64 * kMdWaves) {
+      const int u = base + kMdWaves * lane + wave;
+      const bool open = u < units && (u >= kDoneBits || ((done[u >> 5] >> (u & 31)) & 1u) == 0u);
+      uint64_t todo = __ballot(open);
+      while (todo != 0ull) {
+        const int ua = base + kMdWaves * __builtin_ctzll(todo) + wave;
+        todo &= todo - 1;
+        int ub = -1;
+        if (todo != 0ull) {
+          ub = base + kMdWaves * __builtin_ctzll(todo) + wave;
+          todo &= todo - 1;
+        }
+        int n, n2;
+        sparse_unit_blocks(indices, seqlens, s_q, topk, ua, ub, vec4 != 0, lane, &n, &n2);
+        if (lane == 0) {
+          unit_blocks[ua] = n;
+          cost += n + c0;
+          if (ub >= 0) {
+            unit_blocks[ub] = n2;
+            cost += n2 + c0;
+          }
         }
       }
     }

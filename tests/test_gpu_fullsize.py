@@ -33,7 +33,8 @@ def _sample_rows(inp, n, seed):
     return np.array(sorted(pick), dtype=np.int32)
 
 
-@pytest.mark.parametrize("name,seed", [("membound", 901), ("mtp", 902), ("fp8", 903), ("sparse", 904)])
+@pytest.mark.parametrize("name,seed", [("membound", 901), ("mtp", 902), ("fp8", 903), ("sparse", 904),
+                                       ("sparse_prefill", 905)])
 def test_full_size_sampled_rows(oracle_mod, name, seed):
     cfg = gen.WORKLOADS[name]
     log(f"full-size {cfg.name}")

@@ -136,6 +136,20 @@ def test_sparse_schedule_finds_last_valid_entry_anywhere(topk):
         assert np.array_equal(md.num_splits.cpu().numpy(), ref_ns), P
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_sparse_prefill_shape(oracle_mod, fmt):
+    """Many query tokens per sequence, each with its own top-k list drawn
+    from its causal window (prefill), against the oracle on every row."""
+    cfg = gen.small_config(2, 48, 128, [600, 1000], causal=True, fmt=fmt, topk=256, seed=61,
+                           topk_in_window=True)
+    inp = gen.make_inputs(cfg, poison=True, extra_pages=1)
+    log(f"sparse prefill fmt={fmt}")
+    for parts in (None, 24):
+        o, l, _ = run_gpu(inp, num_parts=parts)
+        ro, rl = oracle_mod.decode(inp)
+        compare(o, l, ro, rl, fmt, f"sparse prefill fmt={fmt} parts={parts}")
+
+
 def test_single_key_returns_v_row_bitwise():
     cfg = gen.small_config(3, 1, 16, [1, 1, 1], seed=41)
     inp = gen.make_inputs(cfg, poison=True)
