@@ -324,6 +324,7 @@ KERNEL_NAMES = {
     "fp8": "void mla::wide::wide_kernel<1, false>(mla::DecodeParams)",
     "sparse": "void mla::wide::wide_kernel<1, true>(mla::DecodeParams)",
     "sparse_prefill": "void mla::wide::wide_kernel<1, true>(mla::DecodeParams)",
+    "dense_prefill": "mla::wide::offset_kernel(mla::DecodeParams)",
 }
 KERNEL_SOURCES = {
     "membound": ["mla_decode_narrow.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
@@ -331,6 +332,7 @@ KERNEL_SOURCES = {
     "fp8": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
     "sparse": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
     "sparse_prefill": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+    "dense_prefill": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "narrow_kernel_membound_b64_h16_traffic.md")
 # Kernel trace + MFMA counter summaries of the compute-bound workloads.
@@ -423,10 +425,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true",
                     help="skip the MTP, FP8 and sparse workloads")
-    ap.add_argument("--only", choices=["mtp", "fp8", "sparse", "sparse_prefill", "append"], default=None,
+    ap.add_argument("--only", choices=["mtp", "fp8", "sparse", "sparse_prefill", "dense_prefill", "append"],
+                    default=None,
                     help="time just this secondary workload (for profiling)")
     ap.add_argument("--pmc-run", nargs="?", const="membound", default=None,
-                    choices=["membound", "mtp", "fp8", "sparse", "sparse_prefill"],
+                    choices=["membound", "mtp", "fp8", "sparse", "sparse_prefill", "dense_prefill"],
                     help="the run hardware counters are collected on (no timing)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -503,7 +506,7 @@ def main():
                                                 if k in traffic}
     if not args.only_primary:
         extra = {}
-        for key in ("mtp", "fp8", "sparse", "sparse_prefill"):
+        for key in ("mtp", "fp8", "sparse", "sparse_prefill", "dense_prefill"):
             del prim
             torch.cuda.empty_cache()
             log(f"[bench] timing {key}")

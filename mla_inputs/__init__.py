@@ -67,7 +67,7 @@ class Config:
 
 
 # The five workloads the decode is measured and checked on, by short name.
-# Seeds: 1000 for tiny, then 1001 .. 1005 in the order listed.
+# Seeds: 1000 for tiny, then 1001 .. 1006 in the order listed.
 WORKLOADS = {
     "tiny": Config("tiny_b2_h16", batch=2, s_q=1, h_q=16, seqlens=[37, 130],
                    seed=1000),
@@ -85,6 +85,10 @@ WORKLOADS = {
     "sparse_prefill": Config("sparse_prefill_fp8_b1_sq2048_h128_L8192_top2048", batch=1, s_q=2048,
                              h_q=128, seqlens=8192, causal=True, fmt=FMT_FP8, topk=2048,
                              topk_in_window=True, seed=1005),
+    # Dense prefill: the same 2048 new tokens attending to their whole
+    # causal window, bf16 rows.
+    "dense_prefill": Config("dense_prefill_bf16_b1_sq2048_h128_L8192", batch=1, s_q=2048, h_q=128,
+                            seqlens=8192, causal=True, seed=1006),
 }
 
 

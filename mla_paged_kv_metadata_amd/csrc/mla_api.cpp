@@ -59,13 +59,16 @@ int units_of(int batch, int s_q, int topk) { return topk > 0 ? batch * s_q : bat
 int rows_per_unit(int s_q, int h_q, int topk) { return topk > 0 ? h_q : s_q * h_q; }
 
 // One decode workgroup per compute unit: P * row_tiles ~= #CUs, P a
-// multiple of 8 (whole XCD groups), at least 8.
+// multiple of 8 (whole XCD groups) when that leaves at least 8 parts.
+// With more row tiles than that (many query rows per sequence, e.g. a
+// prefill) the tiles fill the device by themselves: fewer parts, down to
+// 1 (no key splits at all) once there is a tile per compute unit.
 int auto_parts(int rows, int cus) {
   const int rt = mla::rows_per_workgroup(rows);
   const int tiles = (rows + rt - 1) / rt;
-  int p = cus / tiles;
-  p = p / 8 * 8;
-  return p < 8 ? 8 : p;
+  const int p = cus / tiles;
+  if (p >= 8) return p / 8 * 8;
+  return p < 1 ? 1 : p;
 }
 
 size_t md_elems(int units, int parts) {

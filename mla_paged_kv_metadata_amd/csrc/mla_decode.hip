@@ -102,8 +102,7 @@ int rows_per_workgroup(int rows_per_unit) { return rows_per_unit <= 32 ? 16 : 12
 
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int which, hipStream_t stream) {
   if (which & 1) {
-    const int parts8 = (p.num_parts + 7) / 8 * 8;
-    const dim3 grid(parts8 * p.row_tiles);
+    const dim3 grid(decode_grid(p.num_parts, p.row_tiles));
     const hipError_t e = rows_per_workgroup(p.R) == 128 ? launch_wide(p, kv_format, grid, stream)
                                                          : launch_narrow(p, kv_format, grid, stream);
     if (e != hipSuccess) return e;

@@ -117,10 +117,8 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
 
   // Work item: XCD-aware (consecutive block ids go to different XCDs, the
   // row tiles of one part share an XCD and its L2).
-  const int bid = blockIdx.x;
-  const int rest = bid >> 3;
-  const int rt = rest % p.row_tiles;
-  const int part = (rest / p.row_tiles) * 8 + (bid & 7);
+  int part, rt;
+  work_item(blockIdx.x, p.num_parts, p.row_tiles, &part, &rt);
   if (part >= p.num_parts) return;
   // Header and part row are read together (one round trip).
   const int32_t* prow = p.md + kHeader + kPartRow * part;

@@ -397,6 +397,16 @@ __device__ __forceinline__ void store_unit(const DecodeParams& p, const f32x16 (
   }
 }
 
+// Dense causal units: the block after the last key any row of 128-row
+// tile rt may see (its last row has the widest window).  Blocks from there
+// on are skipped; one block is always kept so that the unit still runs
+// through its epilogue (its rows then see no key of this part).
+__device__ __forceinline__ int causal_tile_end(const DecodeParams& p, int rt, int L, int jb, int je) {
+  const int last_row = min(rt * kRowsPerWg + kRowsPerWg - 1, p.R - 1);
+  const int W = min(max(L - p.s_q + 1 + last_row / p.h_q, 0), L);
+  return min(je, max(jb + 1, (W + kPage - 1) / kPage));
+}
+
 // Work-item decode shared by both kernels (XCD-aware: consecutive block ids
 // go to different XCDs, the row tiles of one part share an XCD and its L2).
 struct Item {
@@ -404,10 +414,7 @@ struct Item {
   const int32_t* unit_blocks;
 };
 __device__ __forceinline__ bool decode_item(const DecodeParams& p, Item& it) {
-  const int bid = blockIdx.x;
-  const int rest = bid >> 3;
-  it.rt = rest % p.row_tiles;
-  it.part = (rest / p.row_tiles) * 8 + (bid & 7);
+  work_item(blockIdx.x, p.num_parts, p.row_tiles, &it.part, &it.rt);
   if (it.part >= p.num_parts) return false;
   if (p.md[0] != p.num_parts || p.md[5] != kMagic || p.md[3] != p.units) return false;
   const int32_t* prow = p.md + kHeader + kPartRow * it.part;
@@ -453,9 +460,10 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
 
   for (int u = it.u0; u <= it.u1; ++u) {
     const int jb = (u == it.u0) ? it.j0 : 0;
-    const int je = (u == it.u1) ? it.j1 : it.unit_blocks[u];
+    const int je_part = (u == it.u1) ? it.j1 : it.unit_blocks[u];
     const int b = SPARSE ? u / p.s_q : u;
     const int L = p.seqlens[b];
+    const int je = (SPARSE || !p.causal) ? je_part : causal_tile_end(p, it.rt, L, jb, je_part);
     const int s_unit = SPARSE ? u % p.s_q : 0;
     const int s_row = SPARSE ? s_unit : (row_ok ? my_row / p.h_q : 0);
     const int W = p.causal ? min(max(L - p.s_q + 1 + s_row, 0), L) : L;
@@ -581,9 +589,10 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
 
   for (int u = it.u0; u <= it.u1; ++u) {
     const int jb = (u == it.u0) ? it.j0 : 0;
-    const int je = (u == it.u1) ? it.j1 : it.unit_blocks[u];
+    const int je_part = (u == it.u1) ? it.j1 : it.unit_blocks[u];
     const int b = u;
     const int L = p.seqlens[b];
+    const int je = p.causal ? causal_tile_end(p, it.rt, L, jb, je_part) : je_part;
     const int s_row = row_ok ? my_row / p.h_q : 0;
     const int W = p.causal ? min(max(L - p.s_q + 1 + s_row, 0), L) : L;
     const int W_lo = p.causal ? min(max(L - p.s_q + 1, 0), L) : L;

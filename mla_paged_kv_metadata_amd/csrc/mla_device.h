@@ -67,6 +67,29 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Work item (part, row tile) of workgroup bid.  With eight or more parts
+// the grid holds the parts rounded up to a multiple of 8 times the row
+// tiles, and consecutive block ids (which go to different XCDs) take
+// consecutive parts, the row tiles of one part sharing an XCD and its L2:
+// part = (rest / row_tiles) * 8 + (bid & 7), tile = rest % row_tiles with
+// rest = bid / 8.  With fewer parts (row tiles alone fill the device) the
+// grid is parts * row_tiles and bid = tile * parts + part.
+__device__ __forceinline__ void work_item(int bid, int num_parts, int row_tiles, int* part, int* tile) {
+  if (num_parts >= 8) {
+    const int rest = bid >> 3;
+    *tile = rest % row_tiles;
+    *part = (rest / row_tiles) * 8 + (bid & 7);
+  } else {
+    *tile = bid / num_parts;
+    *part = bid - *tile * num_parts;
+  }
+}
+
+// Grid size for the mapping above.
+inline int decode_grid(int num_parts, int row_tiles) {
+  return (num_parts >= 8 ? (num_parts + 7) / 8 * 8 : num_parts) * row_tiles;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);

@@ -34,7 +34,7 @@ def _sample_rows(inp, n, seed):
 
 
 @pytest.mark.parametrize("name,seed", [("membound", 901), ("mtp", 902), ("fp8", 903), ("sparse", 904),
-                                       ("sparse_prefill", 905)])
+                                       ("sparse_prefill", 905), ("dense_prefill", 906)])
 def test_full_size_sampled_rows(oracle_mod, name, seed):
     cfg = gen.WORKLOADS[name]
     log(f"full-size {cfg.name}")

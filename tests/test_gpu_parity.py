@@ -150,6 +150,24 @@ def test_sparse_prefill_shape(oracle_mod, fmt):
         compare(o, l, ro, rl, fmt, f"sparse prefill fmt={fmt} parts={parts}")
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_dense_prefill_shape(oracle_mod, fmt):
+    """Many query tokens per sequence over the whole causal window (a
+    prefill: 64 new tokens after a 536-token prefix, and a sequence made of
+    its 64 new tokens only), against the oracle on every row.  With 64
+    row tiles the library picks 4 parts (tiles fill the device), and 1 and
+    16 parts are forced too."""
+    cfg = gen.small_config(2, 64, 128, [600, 64], causal=True, fmt=fmt, seed=62)
+    inp = gen.make_inputs(cfg, poison=True, extra_pages=1)
+    ro, rl = oracle_mod.decode(inp)
+    for parts in (None, 1, 16):
+        log(f"dense prefill fmt={fmt} parts={parts}")
+        o, l, md = run_gpu(inp, num_parts=parts)
+        if parts is None:
+            assert md.num_parts < 8
+        compare(o, l, ro, rl, fmt, f"dense prefill fmt={fmt} parts={md.num_parts}")
+
+
 def test_single_key_returns_v_row_bitwise():
     cfg = gen.small_config(3, 1, 16, [1, 1, 1], seed=41)
     inp = gen.make_inputs(cfg, poison=True)
