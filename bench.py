@@ -340,6 +340,8 @@ MFMA_FILES = {
     "mtp": os.path.join(ROOT, "profiles", "offset_kernel_mtp_b128_sq2_h128_kernel_stats.md"),
     "fp8": os.path.join(ROOT, "profiles", "wide_kernel_fp8_b64_h128_L8192_kernel_stats.md"),
     "sparse": os.path.join(ROOT, "profiles", "wide_kernel_sparse_b32_h128_top2048_kernel_stats.md"),
+    "sparse_prefill": os.path.join(ROOT, "profiles", "wide_kernel_sparse_prefill_sq2048_h128_top2048_kernel_stats.md"),
+    "dense_prefill": os.path.join(ROOT, "profiles", "offset_kernel_dense_prefill_sq2048_h128_L8192_kernel_stats.md"),
 }
 
 
