@@ -41,12 +41,6 @@ __device__ __forceinline__ long long wave_inclusive_scan(long long x, int lane) 
   return x;
 }
 
-__device__ __forceinline__ long long wave_sum(long long x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
-}
-
 // Exclusive prefix of v over the workgroup, and the workgroup total.  One
 // barrier; callers alternate between two `sh` buffers so that a buffer is
 // rewritten only after every wave has passed the next call's barrier.
