@@ -162,7 +162,8 @@ int mla_decode_kvcache(const mla_decode_args *args, void *stream);
  * sequences leave partial results in the workspace.  mla_decode_combine
  * enqueues only the merge of those partials (log-sum-exp weighting:
  * lse = log sum_i exp(lse_i), out = sum_i exp(lse_i - lse) * out_i) into
- * out/lse; it must follow mla_decode_partial on the same arguments and
+ * out/lse (with num_parts = 1 no sequence is split and nothing is
+ * enqueued); it must follow mla_decode_partial on the same arguments and
  * workspace.  Same arguments and errors as mla_decode_kvcache.
  */
 int mla_decode_partial(const mla_decode_args *args, void *stream);

@@ -43,12 +43,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
                                                       const float* __restrict__ ws_lse,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse, int R) {
-  const int u = blockIdx.x;
+  // Workgroup = (unit, four rows), flattened so that any row count fits.
+  const int quads = (R + 3) / 4;
+  const int u = blockIdx.x / quads;
   const int base = num_splits[u];
   const int k = num_splits[u + 1] - base;
   if (k <= 1) return;
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int r = (blockIdx.x - u * quads) * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
   const float* lrow = ws_lse + (size_t)base * R + r;
   // Lane i keeps lse_i of the first 64 splits.
@@ -107,8 +109,9 @@ hipError_t launch_decode(const DecodeParams& p, int kv_format, int which, hipStr
                                                          : launch_narrow(p, kv_format, grid, stream);
     if (e != hipSuccess) return e;
   }
-  if (which & 2) {
-    const dim3 cgrid(p.units, (p.R + 3) / 4);
+  // With a single part no unit is split: there is nothing to combine.
+  if ((which & 2) && p.num_parts > 1) {
+    const dim3 cgrid((unsigned)((size_t)p.units * ((p.R + 3) / 4)));
     hipLaunchKernelGGL(combine_kernel, cgrid, dim3(256), 0, stream, p.num_splits, p.ws_o, p.ws_lse,
                        p.out, p.lse, p.R);
     return hipGetLastError();

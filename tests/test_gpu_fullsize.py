@@ -43,3 +43,17 @@ def test_full_size_sampled_rows(oracle_mod, name, seed):
     sel = _sample_rows(inp, 96, seed)
     ro, rl = oracle_mod.decode(inp, sel=sel)
     compare(o[sel], l[sel], ro, rl, inp.fmt, f"{cfg.name} ({len(sel)} rows, {md.num_parts} parts)")
+
+
+def test_prefill_split_in_two_combines_every_row(oracle_mod):
+    """2048 tokens x 128 heads = 262,144 rows in one sequence, forced into
+    two parts: the combine covers more than 65,535 four-row groups."""
+    cfg = gen.small_config(1, 2048, 128, [2048], causal=True, seed=907)
+    log("prefill split in two")
+    inp = gen.make_inputs(cfg)
+    o, l, md = run_gpu(inp, num_parts=2)
+    assert int(md.num_splits[-1]) == 2   # the sequence is split once
+    sel = _sample_rows(inp, 96, 907)
+    sel = np.unique(np.concatenate([sel, np.arange(inp.s_q * inp.h_q - 16, inp.s_q * inp.h_q)])).astype(np.int32)
+    ro, rl = oracle_mod.decode(inp, sel=sel)
+    compare(o[sel], l[sel], ro, rl, inp.fmt, f"prefill split in two ({len(sel)} rows)")
