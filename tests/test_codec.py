@@ -94,3 +94,20 @@ def test_generator_bf16_rounding_matches_torch():
     x = rng.standard_normal(10000, dtype=np.float32) * 100
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(gen.f32_to_bf16_bits(x), ref)
+
+
+def test_generator_block_tables_are_valid():
+    """Every sequence's blocks map to distinct pool pages, unused entries
+    hold -1, and the pages in use cover exactly the needed ones."""
+    for seed, (lens, extra) in enumerate([([37, 130], 0), ([1, 64, 65, 700, 0], 3), ([4096] * 3, 1)]):
+        cfg = gen.small_config(len(lens), 1, 16, lens, seed=300 + seed, max_blocks=80)
+        inp = gen.make_inputs(cfg, extra_pages=extra)
+        need = [(L + 63) // 64 for L in lens]
+        used = []
+        for b, n in enumerate(need):
+            row = inp.block_table[b]
+            assert np.all(row[n:] == -1)
+            assert np.all((row[:n] >= 0) & (row[:n] < inp.num_pages))
+            used.extend(row[:n].tolist())
+        assert len(set(used)) == len(used) == sum(need)
+        assert inp.num_pages == sum(need) + extra
