@@ -151,6 +151,9 @@ int mla_workspace_size(const mla_decode_args *args, size_t *bytes);
  * Enqueues the split-KV attention kernel and the log-sum-exp combine kernel
  * on `stream`.  The metadata must come from mla_get_metadata with the same
  * batch, s_q, h_q * s_q, topk, cache_seqlens, indices and num_parts.
+ * Limits (MLA_ERR_INVALID_ARGUMENT beyond them): batch * s_q * h_q below
+ * 2^31 query rows, and num_parts (rounded up to a multiple of 8 when >= 8)
+ * times the row tiles of one unit below 2^31 workgroups.
  */
 int mla_decode_kvcache(const mla_decode_args *args, void *stream);
 

@@ -2,6 +2,7 @@
 // launches.  Declarations and contracts are in include/mla.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -108,8 +109,19 @@ int check_decode_shape(const mla_decode_args* a) {
     return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts must be in [1, %d]", mla::kMaxParts);
   if (!std::isfinite(a->softmax_scale))
     return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
-  if ((long long)a->batch * a->s_q * a->h_q > (1LL << 31) / mla::kDqk)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "too many query rows");
+  // Row counts are 32-bit in the kernels (every memory offset is 64-bit).
+  if ((long long)std::max(a->batch, 1) * a->s_q * a->h_q > 0x7FFFFFFFLL)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "too many query rows (batch * s_q * h_q must be below 2^31)");
+  {
+    // One workgroup per (part, row tile); the grid is one-dimensional.
+    const int R = rows_per_unit(a->s_q, a->h_q, a->topk);
+    const int rt = mla::rows_per_workgroup(R);
+    const long long tiles = (R + rt - 1) / rt;
+    const long long parts = a->num_parts >= 8 ? (a->num_parts + 7) / 8 * 8 : a->num_parts;
+    if (parts * tiles > 0x7FFFFFFFLL)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts * row tiles (%lld) exceeds the grid limit",
+                  parts * tiles);
+  }
   return MLA_OK;
 }
 

@@ -99,6 +99,23 @@ def test_decode_rejects_bad_arguments_without_launching(lib, field, value, code)
     assert lib.mla_last_error() != b""
 
 
+def test_query_row_and_grid_limits(lib):
+    n = ctypes.c_size_t()
+    # a 32K-token prefill over 128 heads (4.2M query rows) is in range
+    a = _args(batch=1, s_q=32768, h_q=128, causal=1, num_parts=1)
+    assert lib.mla_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value >= 2 * 32768 * 128 * 512 * 2
+    # rows counted in 32 bits: 2^31 rows are refused, also for an empty batch
+    for b in (1, 0):
+        a = _args(batch=b, s_q=1 << 16, h_q=1 << 15)
+        assert lib.mla_decode_kvcache(ctypes.byref(a), None) == -1
+        assert b"query rows" in lib.mla_last_error()
+    # one workgroup per (part, row tile) in a 1-D grid
+    a = _args(batch=1, s_q=1 << 20, h_q=1 << 10, num_parts=2048)
+    assert lib.mla_decode_kvcache(ctypes.byref(a), None) == -1
+    assert b"grid" in lib.mla_last_error()
+
+
 def test_decode_rejects_null_pointers_and_small_workspace(lib):
     a = _args()
     assert lib.mla_decode_kvcache(ctypes.byref(a), None) == -1   # q etc. are NULL
