@@ -31,11 +31,14 @@ namespace {
 
 constexpr int kMdThreads = 1024;
 constexpr int kMdWaves = kMdThreads / 64;
+constexpr int kUnitCache = 4096;                 // units whose count and length stay in LDS
+constexpr int kSmallSparse = 4 * kMdWaves;       // sparse units read in a single pass
 
-__device__ __forceinline__ long long wave_inclusive_scan(long long x, int lane) {
+template <typename V>
+__device__ __forceinline__ V wave_inclusive_scan(V x, int lane) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const long long y = __shfl_up(x, d);
+    const V y = __shfl_up(x, d);
     if (lane >= d) x += y;
   }
   return x;
@@ -44,14 +47,15 @@ __device__ __forceinline__ long long wave_inclusive_scan(long long x, int lane) 
 // Exclusive prefix of v over the workgroup, and the workgroup total.  One
 // barrier; callers alternate between two `sh` buffers so that a buffer is
 // rewritten only after every wave has passed the next call's barrier.
-__device__ __forceinline__ long long wg_exclusive_scan(long long v, long long* sh, long long* total) {
+template <typename V>
+__device__ __forceinline__ V wg_exclusive_scan(V v, V* sh, V* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const long long incl = wave_inclusive_scan(v, lane);
+  const V incl = wave_inclusive_scan(v, lane);
   if (lane == 63) sh[wave] = incl;
   __syncthreads();
-  const long long wt = wave_inclusive_scan(lane < kMdWaves ? sh[lane] : 0, lane);
+  const V wt = wave_inclusive_scan(lane < kMdWaves ? sh[lane] : V(0), lane);
   *total = __shfl(wt, kMdWaves - 1);
-  const long long before = wave > 0 ? __shfl(wt, wave - 1) : 0;
+  const V before = wave > 0 ? __shfl(wt, wave - 1) : V(0);
   return before + incl - v;
 }
 
@@ -161,6 +165,66 @@ __device__ __forceinline__ int dense_unit_blocks(int L) {
 
 }  // namespace
 
+// Unit positions on the cost line, split counts and the part rows, 1024
+// units at a time (Pos: the integer type of cost positions).  Part indices
+// stay below kMaxParts and fit an int.
+template <bool SPARSE, typename Pos>
+__device__ __forceinline__ void place_units(const int32_t* __restrict__ seqlens, const int32_t* unit_blocks,
+                                            const int32_t* ucnt, const int32_t* ulen, int s_q, int units, Pos T,
+                                            int32_t* rows, int32_t* __restrict__ num_splits, Pos (*sh)[kMdWaves]) {
+  const int tid = threadIdx.x;
+  const Pos c0 = kUnitOverhead;
+  Pos carry_c = 0, carry_k = 0;
+  for (int base = 0; base < units; base += kMdThreads) {
+    const int u = base + tid;
+    const bool live = u < units;
+    Pos nb = 0;
+    int Lu = 0;
+    if (live) {
+      if (u < kUnitCache) {
+        Lu = ulen[u];
+        nb = SPARSE ? ucnt[u] : dense_unit_blocks(Lu);
+      } else {
+        Lu = seqlens[SPARSE ? u / s_q : u];
+        nb = SPARSE ? unit_blocks[u] : dense_unit_blocks(Lu);
+      }
+    }
+    const Pos c = live ? nb + c0 : 0;
+    Pos chunk_c, chunk_k;
+    const Pos Cu = carry_c + wg_exclusive_scan(c, sh[1], &chunk_c);
+    int f = 0, l = -1;
+    if (live) {
+      f = (int)((Cu + c0) / T);
+      l = (int)((Cu + c0 + nb - 1) / T);
+    }
+    const Pos k = live ? (Pos)(l - f + 1) : 0;
+    const Pos Ku = carry_k + wg_exclusive_scan(k, sh[0], &chunk_k);
+    if (live) {
+      num_splits[u + 1] = (int32_t)(Ku + k);
+      // Parts whose first unit is u: those of u's parts that the previous
+      // unit (whose last block sits at position Cu - 1) does not reach.
+      const int lo = u > 0 ? max(f, (int)((Cu - 1) / T) + 1) : f;
+      for (int pp = lo; pp <= l; ++pp) {
+        int32_t* row = rows + kPartRow * pp;
+        row[0] = u;
+        row[1] = (int32_t)(pp == f ? 0 : (Pos)pp * T - Cu - c0);
+        row[4] = pp - f;
+        row[5] = Lu;
+        row[6] = (int32_t)nb;
+      }
+      // Parts whose last unit is u: those the next unit does not start in.
+      const int hi = (u + 1 < units) ? min(l, (int)((Cu + c + c0) / T) - 1) : l;
+      for (int pp = f; pp <= hi; ++pp) {
+        int32_t* row = rows + kPartRow * pp;
+        row[2] = u;
+        row[3] = (int32_t)(pp == l ? nb : (Pos)(pp + 1) * T - Cu - c0);
+      }
+    }
+    carry_c += chunk_c;
+    carry_k += chunk_k;
+  }
+}
+
 template <bool SPARSE>
 __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __restrict__ seqlens,
                                                               const int32_t* __restrict__ indices,
@@ -168,11 +232,16 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
                                                               int num_parts, int32_t* __restrict__ md,
                                                               int32_t* __restrict__ num_splits) {
   __shared__ long long sh[2][kMdWaves];
+  __shared__ uint32_t sh32[2][kMdWaves];
   __shared__ int32_t rows[kMaxParts * kPartRow];
   // Sparse: bit u set when unit u's block count is known from its last
   // index entry alone (units below kDoneBits).
   constexpr int kDoneBits = SPARSE ? 65536 : 32;
   __shared__ uint32_t done[kDoneBits / 32];
+  // Block counts and sequence lengths of units below kUnitCache, kept here
+  // so that the positions pass below reads no global memory for them.
+  __shared__ int32_t ucnt[kUnitCache];
+  __shared__ int32_t ulen[kUnitCache];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = num_parts;
   const long long c0 = kUnitOverhead;
@@ -186,7 +255,37 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
 
   // Block counts and the total cost.
   long long cost = 0;
-  if (SPARSE) {
+  if (SPARSE && units <= kSmallSparse) {
+    // Few units: wave w takes units w, w + 16, w + 32 and w + 48 and loads
+    // the last 256 entries of all of them at once; a row is scanned further
+    // only when none of those entries points into its sequence.
+    Tail t[kSmallSparse / kMdWaves];
+    int L[kSmallSparse / kMdWaves];
+#pragma unroll
+    for (int k = 0; k < kSmallSparse / kMdWaves; ++k) {
+      const int u = wave + kMdWaves * k;
+      if (u < units) {
+        L[k] = seqlens[u / s_q];
+        t[k] = load_tail(indices + (size_t)u * topk, topk, vec4 != 0, lane);
+      }
+    }
+    const int rest = topk > kTail ? topk - kTail : 0;
+#pragma unroll
+    for (int k = 0; k < kSmallSparse / kMdWaves; ++k) {
+      const int u = wave + kMdWaves * k;
+      if (u < units) {
+        int last = tail_last(t[k], topk, L[k], lane);
+        if (last < 0 && rest > 0) last = last_valid_in(indices + (size_t)u * topk, 0, rest, L[k], vec4 != 0, lane);
+        const int n = max(1, (last + 1 + kPage - 1) / kPage);
+        if (lane == 0) {
+          unit_blocks[u] = n;
+          ucnt[u] = n;
+          ulen[u] = L[k];
+          cost += n + c0;
+        }
+      }
+    }
+  } else if (SPARSE) {
     for (int i = tid; i < kDoneBits / 32; i += kMdThreads) done[i] = 0u;
     __syncthreads();
     // A row whose last entry points into the sequence spans all its blocks
@@ -194,8 +293,11 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
     const int n_all = (topk + kPage - 1) / kPage;
     for (int u = tid; u < units; u += kMdThreads) {
       const int last = indices[(size_t)u * topk + topk - 1];
-      if (last >= 0 && last < seqlens[u / s_q]) {
+      const int Lu = seqlens[u / s_q];
+      if (u < kUnitCache) ulen[u] = Lu;
+      if (last >= 0 && last < Lu) {
         unit_blocks[u] = n_all;
+        if (u < kUnitCache) ucnt[u] = n_all;
         cost += n_all + c0;
         if (u < kDoneBits) atomicOr(&done[u >> 5], 1u << (u & 31));
       }
@@ -221,73 +323,38 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
         sparse_unit_blocks(indices, seqlens, s_q, topk, ua, ub, vec4 != 0, lane, &n, &n2);
         if (lane == 0) {
           unit_blocks[ua] = n;
+          if (ua < kUnitCache) ucnt[ua] = n;
           cost += n + c0;
           if (ub >= 0) {
             unit_blocks[ub] = n2;
+            if (ub < kUnitCache) ucnt[ub] = n2;
             cost += n2 + c0;
           }
         }
       }
     }
-    // The counts are read back by other waves of this workgroup after the
-    // barrier in the scan below, which orders these stores before them.
   } else {
     for (int u = tid; u < units; u += kMdThreads) {
-      const int n = dense_unit_blocks(seqlens[u]);
+      const int Lu = seqlens[u];
+      const int n = dense_unit_blocks(Lu);
+      if (u < kUnitCache) ulen[u] = Lu;
       unit_blocks[u] = n;
       cost += n + c0;
     }
   }
+  // Counts and lengths of units at or above kUnitCache are read back from
+  // global memory below; the barrier in the scan orders them (and the LDS
+  // entries) after these stores.
   long long tot_cost;
   wg_exclusive_scan(cost, sh[0], &tot_cost);
   const long long T = tot_cost > 0 ? (tot_cost + P - 1) / P : 1;
   const long long tot_blocks = tot_cost - c0 * units;
-
-  // Unit positions, split counts and the part rows, 1024 units at a time.
-  long long carry_c = 0, carry_k = 0;
-  for (int base = 0; base < units; base += kMdThreads) {
-    const int u = base + tid;
-    const bool live = u < units;
-    long long nb = 0;
-    int Lu = 0;
-    if (live) {
-      Lu = seqlens[SPARSE ? u / s_q : u];
-      nb = SPARSE ? unit_blocks[u] : dense_unit_blocks(Lu);
-    }
-    const long long c = live ? nb + c0 : 0;
-    long long chunk_c, chunk_k;
-    const long long Cu = carry_c + wg_exclusive_scan(c, sh[1], &chunk_c);
-    long long f = 0, l = -1;
-    if (live) {
-      f = (Cu + c0) / T;
-      l = (Cu + c0 + nb - 1) / T;
-    }
-    const long long k = live ? l - f + 1 : 0;
-    const long long Ku = carry_k + wg_exclusive_scan(k, sh[0], &chunk_k);
-    if (live) {
-      num_splits[u + 1] = (int32_t)(Ku + k);
-      // Parts whose first unit is u: those of u's parts that the previous
-      // unit (whose last block sits at position Cu - 1) does not reach.
-      const long long lo = u > 0 ? max(f, (Cu - 1) / T + 1) : f;
-      for (long long p = lo; p <= l; ++p) {
-        int32_t* row = rows + kPartRow * p;
-        row[0] = u;
-        row[1] = (int32_t)(p == f ? 0 : p * T - Cu - c0);
-        row[4] = (int32_t)(p - f);
-        row[5] = Lu;
-        row[6] = (int32_t)nb;
-      }
-      // Parts whose last unit is u: those the next unit does not start in.
-      const long long hi = (u + 1 < units) ? min(l, (Cu + c + c0) / T - 1) : l;
-      for (long long p = f; p <= hi; ++p) {
-        int32_t* row = rows + kPartRow * p;
-        row[2] = u;
-        row[3] = (int32_t)(p == l ? nb : (p + 1) * T - Cu - c0);
-      }
-    }
-    carry_c += chunk_c;
-    carry_k += chunk_k;
-  }
+  // Positions in 32 bits whenever the whole cost line allows it (then
+  // P * T < 2^31 + P as well): the divisions by T are then short.
+  if (tot_cost < (1LL << 31))
+    place_units<SPARSE, uint32_t>(seqlens, unit_blocks, ucnt, ulen, s_q, units, (uint32_t)T, rows, num_splits, sh32);
+  else
+    place_units<SPARSE, long long>(seqlens, unit_blocks, ucnt, ulen, s_q, units, T, rows, num_splits, sh);
   __syncthreads();
 
   if (tid == 0) {
@@ -305,19 +372,8 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
   for (int i = tid; i < P * kPartRow; i += kMdThreads) md[kHeader + i] = rows[i];
 }
 
-// Dense schedule for at most 64 units: one wave, one unit per lane, the
-// same arithmetic as metadata_kernel without its workgroup scans.
-// Inclusive wave scan of 32-bit values.
-__device__ __forceinline__ uint32_t wave_inclusive_scan32(uint32_t x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
-
-// Dense schedules of at most 64 units: one wave, one lane per unit.  With
+// Dense schedules of at most 64 units: one wave, one lane per unit, the
+// same arithmetic as metadata_kernel without its workgroup scans.  With
 // n_u <= 2^25 (L_b < 2^31) and at most 64 units every cost position is
 // below 2^32, so the cost line is kept in 32-bit unsigned arithmetic.
 __global__ __launch_bounds__(64) void metadata_wave_kernel(const int32_t* __restrict__ seqlens, int units,
@@ -339,7 +395,7 @@ __global__ __launch_bounds__(64) void metadata_wave_kernel(const int32_t* __rest
   const uint32_t nb = live ? (uint32_t)dense_unit_blocks(Lu) : 0u;
   if (live) unit_blocks[lane] = (int32_t)nb;
   const uint32_t c = live ? nb + c0 : 0u;
-  const uint32_t incl = wave_inclusive_scan32(c, lane);
+  const uint32_t incl = wave_inclusive_scan<uint32_t>(c, lane);
   const uint32_t tot_cost = __shfl(incl, 63);
   const uint32_t T = tot_cost > 0 ? (tot_cost - 1) / (uint32_t)P + 1 : 1u;
   const uint32_t Cu = incl - c;
@@ -350,7 +406,7 @@ __global__ __launch_bounds__(64) void metadata_wave_kernel(const int32_t* __rest
     l = (int)((Cu + c0 + nb - 1) / T);
   }
   const uint32_t k = live ? (uint32_t)(l - f + 1) : 0u;
-  const uint32_t kincl = wave_inclusive_scan32(k, lane);
+  const uint32_t kincl = wave_inclusive_scan<uint32_t>(k, lane);
   __syncthreads();   // row defaults before the rows below
   if (live) {
     num_splits[lane + 1] = (int32_t)kincl;

@@ -101,6 +101,112 @@ def test_schedule_matches_oracle_bitwise():
         S.check_schedule(ref_md, ref_ns, nb)
 
 
+@pytest.mark.parametrize("units,sparse", [(1, True), (63, True), (64, True), (65, True), (4096, True),
+                                          (4097, True), (65, False), (4096, False), (4097, False),
+                                          (6000, False)])
+def test_schedule_unit_count_boundaries(units, sparse):
+    """Unit counts on both sides of the schedule kernel's switches: at most
+    64 sparse units read in one pass, and the first 4096 units' counts and
+    lengths kept on chip (the rest read back from memory).  Sparse rows get
+    masked tails of random length so that some need the longer scan."""
+    from oracle import splitkv_schedule as S
+    import torch as T
+    from mla_paged_kv_metadata_amd import get_mla_metadata
+    rng = np.random.default_rng(1000 + units + sparse)
+    s_q = 1
+    if sparse:
+        s_q = 3 if units % 3 == 0 else 1
+    b = units // s_q
+    sl = rng.integers(0, 9000, size=b).astype(np.int32)
+    idx = None
+    if sparse:
+        topk = 520 if units <= 65 else 132
+        ind = rng.integers(0, 9000, size=(b, s_q, topk)).astype(np.int32) % np.maximum(sl, 1)[:, None, None]
+        cut = rng.integers(0, topk + 1, size=(b, s_q))
+        for i in range(b):
+            for s in range(s_q):
+                if rng.random() < 0.5:
+                    ind[i, s, cut[i, s]:] = -1
+        idx = T.from_numpy(ind).cuda()
+        nb = S.unit_blocks_sparse(sl, ind)
+    else:
+        nb = S.unit_blocks_dense(sl)
+    log(f"schedule boundary units={units} sparse={sparse}")
+    for P in (8, 256, 2048):
+        md = get_mla_metadata(T.from_numpy(sl).cuda(), s_q * 16, 1, s_q=s_q, indices=idx, num_parts=P)
+        T.cuda.synchronize()
+        ref_md, ref_ns = S.schedule(nb, P, 2, unit_len=np.repeat(sl, s_q) if sparse else sl)
+        assert np.array_equal(md.tile_metadata.cpu().numpy(), ref_md), P
+        assert np.array_equal(md.num_splits.cpu().numpy(), ref_ns), P
+
+
+def _schedule_by_positions(nb, P, c0, unit_len):
+    """The schedule's rows and split counts from its definition (block j of
+    unit u sits at position C_u + c0 + j and belongs to part pos // T),
+    evaluated per part at its two boundary positions in int64 instead of
+    walking every block, so that it reaches cost lines past 2^31."""
+    nb = np.asarray(nb, dtype=np.int64)
+    C = np.concatenate([[0], np.cumsum(nb + c0)[:-1]])
+    total = int(nb.sum()) + c0 * len(nb)
+    T = max(1, -(-total // P)) if total > 0 else 1
+    first = C + c0
+    f, l = first // T, (first + nb - 1) // T
+    ns = np.concatenate([[0], np.cumsum(l - f + 1)]).astype(np.int32)
+    md = np.zeros(8 + 8 * P + len(nb), dtype=np.int64)
+    md[:8] = [P, T, c0, len(nb), int(nb.sum()), 0x4D4C4131, 0, 0]
+    md[8 + 8 * P:] = nb
+    for p in range(P):
+        us = np.nonzero((f <= p) & (l >= p))[0]
+        row = [-1, 0, -1, 0, 0, 0, 0, 0]
+        if us.size:
+            u0, u1 = int(us[0]), int(us[-1])
+            row = [u0, max(0, p * T - int(first[u0])), u1, min(int(nb[u1]), (p + 1) * T - int(first[u1])),
+                   p - int(f[u0]), int(unit_len[u0]), int(nb[u0]), 0]
+        md[8 + 8 * p: 16 + 8 * p] = row
+    return md.astype(np.int32), ns
+
+
+def test_schedule_by_positions_matches_the_walk():
+    """Pins the boundary-position evaluation above to the oracle's walk."""
+    from oracle import splitkv_schedule as S
+    rng = np.random.default_rng(4242)
+    for trial in range(40):
+        U = int(rng.integers(1, 60))
+        nb = rng.integers(1, 300, size=U) if trial % 2 else rng.integers(1, 4, size=U)
+        P = int(rng.choice([1, 3, 8, 64, 255, 2048]))
+        ul = rng.integers(0, 20000, size=U)
+        want_md, want_ns = S.schedule(nb, P, 2, unit_len=ul)
+        got_md, got_ns = _schedule_by_positions(nb, P, 2, ul)
+        assert np.array_equal(got_md, want_md) and np.array_equal(got_ns, want_ns), trial
+
+
+@pytest.mark.parametrize("units,last_blocks", [(65, 61), (65, 62), (4000, None)])
+def test_schedule_cost_line_at_2_31(units, last_blocks):
+    """Cost lines that end at 2^31 - 1, exactly 2^31, and past it (4000
+    units in four scan chunks, fewer than 2^31 blocks but more than 2^31
+    positions): the schedule kernel switches from 32-bit to 64-bit
+    positions at 2^31.  Schedule only: the decode itself is not run at
+    these lengths."""
+    import torch as T
+    from mla_paged_kv_metadata_amd import get_mla_metadata
+    if last_blocks is not None:
+        n = np.full(units, (1 << 25) - 3, dtype=np.int64)
+        n[-1] = last_blocks
+        assert int(n.sum()) + 2 * units - (1 << 31) == last_blocks - 62
+    else:
+        n = np.full(units, ((1 << 31) - units) // units, dtype=np.int64)
+        assert n.sum() < (1 << 31) <= n.sum() + 2 * units
+    sl = (64 * n).astype(np.int32)
+    sl[3] -= 17                          # a partial last block
+    log(f"cost line near 2^31: {units} units, {int(n.sum()) + 2 * units} positions")
+    for P in (8, 1000, 2048):
+        md = get_mla_metadata(T.from_numpy(sl).cuda(), 16, 1, num_parts=P)
+        T.cuda.synchronize()
+        want_md, want_ns = _schedule_by_positions(n, P, 2, sl)
+        assert np.array_equal(md.tile_metadata.cpu().numpy(), want_md), P
+        assert np.array_equal(md.num_splits.cpu().numpy(), want_ns), P
+
+
 @pytest.mark.parametrize("topk", [2048, 1001, 200])
 def test_sparse_schedule_finds_last_valid_entry_anywhere(topk):
     """Block counts of sparse units whose last valid entry lies in the last
