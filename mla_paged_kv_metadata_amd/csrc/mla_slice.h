@@ -164,28 +164,38 @@ __device__ __forceinline__ const uint8_t* bf16_copy_src(const DecodeParams& p, i
 // Dequantise a raw FP8 slice into a bf16 slice (all THREADS threads).
 template <int THREADS>
 __device__ __forceinline__ void dequant_slice(const uint8_t* raw, uint8_t* dst) {
-  // 32 keys x (32 NoPE chunks of 16 codes + 8 RoPE chunks of 8 bf16)
-  for (int w = threadIdx.x; w < kSlice * 40; w += THREADS) {
-    const int t = w / 40;
-    const int k = w - t * 40;
+  static_assert((kSlice * 32) % THREADS == 0 && THREADS % 64 == 0, "whole items per thread");
+  // NoPE: item w is 16-code chunk k = w / 32 of key t = w % 32, so that a
+  // wave's lanes read 32 rows at one offset (the 656-byte row stride puts
+  // 16 lanes on 64 distinct banks) and write one chunk of 32 keys (the
+  // pattern the swizzle keeps conflict-free).  Every thread takes the same
+  // number of items and no lane branches.  One item at a time: the callers
+  // hold all their accumulators across this.
+#pragma unroll 1
+  for (int i = 0; i < kSlice * 32 / THREADS; ++i) {
+    const int w = threadIdx.x + THREADS * i;
+    const int t = w & (kSlice - 1);
+    const int k = w >> 5;
     const uint8_t* rrow = raw + t * kFp8RowBytes;
-    if (k < 32) {
-      const u32x4 codes = *(const u32x4*)(rrow + 16 * k);
-      const float s = *(const float*)(rrow + kFp8ScaleOff + 4 * (k >> 3));
-      uint32_t wv[8];
+    const u32x4 codes = *(const u32x4*)(rrow + 16 * k);
+    const float s = *(const float*)(rrow + kFp8ScaleOff + 4 * (k >> 3));
+    uint32_t wv[8];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[qq], false);
-        const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[qq], true);
-        wv[2 * qq] = pack_bf16x2(a[0] * s, a[1] * s);
-        wv[2 * qq + 1] = pack_bf16x2(c2[0] * s, c2[1] * s);
-      }
-      *(u32x4*)(dst + slice_off(t, 2 * k)) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-      *(u32x4*)(dst + slice_off(t, 2 * k + 1)) = u32x4{wv[4], wv[5], wv[6], wv[7]};
-    } else {
-      const int rc = k - 32;
-      *(u32x4*)(dst + slice_off(t, 64 + rc)) = *(const u32x4*)(rrow + kFp8RopeOff + 16 * rc);
+    for (int qq = 0; qq < 4; ++qq) {
+      const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[qq], false);
+      const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[qq], true);
+      wv[2 * qq] = pack_bf16x2(a[0] * s, a[1] * s);
+      wv[2 * qq + 1] = pack_bf16x2(c2[0] * s, c2[1] * s);
     }
+    *(u32x4*)(dst + slice_off(t, 2 * k)) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    *(u32x4*)(dst + slice_off(t, 2 * k + 1)) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+  }
+  // RoPE: 8 chunks of 8 bf16 per key, copied; item w is chunk w / 32 of key
+  // w % 32 (whole waves take part or skip).
+  for (int w = threadIdx.x; w < kSlice * 8; w += THREADS) {
+    const int t = w & (kSlice - 1);
+    const int rc = w >> 5;
+    *(u32x4*)(dst + slice_off(t, 64 + rc)) = *(const u32x4*)(raw + t * kFp8RowBytes + kFp8RopeOff + 16 * rc);
   }
 }
 
