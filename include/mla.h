@@ -205,8 +205,9 @@ int mla_validate_inputs(const mla_decode_args *args, void *stream);
  *           latent rows, RoPE already applied to dims 512..575.
  *   slots:  [n] int32 (device): token i goes to pool row slots[i] =
  *           page * 64 + position in page; a slot outside [0, num_pages * 64)
- *           (e.g. -1) writes nothing.  Two tokens with the same slot: one of
- *           them is written, which one is unspecified.
+ *           (e.g. -1) writes nothing.  Slots must be distinct: two tokens
+ *           with the same slot leave that row unspecified (their stores may
+ *           interleave, e.g. one token's codes with the other's scales).
  *   kv_format: MLA_KV_BF16 copies the 1152-byte row.  MLA_KV_FP8_656
  *           quantises: per group of 128 NoPE values scale = amax / 448 (fp32;
  *           448 is the largest e4m3fn magnitude), code = x / scale rounded

@@ -247,6 +247,7 @@ def append_kv(rows: torch.Tensor, slots: torch.Tensor, kcache: torch.Tensor) -> 
     """Write token i of rows ([n, 576] bf16) into pool row slots[i]
     (page * 64 + position; outside the pool: skipped) of kcache, as a bf16
     row or a quantised 656-byte FP8 row depending on kcache's format.
+    Slots must be distinct (a repeated slot leaves its row unspecified).
     Returns kcache."""
     if rows.dim() != 2 or rows.shape[1] != D_QK or rows.dtype != torch.bfloat16 or not rows.is_contiguous():
         raise ValueError("rows must be a contiguous bf16 [n, 576] tensor")
