@@ -57,6 +57,9 @@ int current_cu_count(int* cus) {
 
 int units_of(int batch, int s_q, int topk) { return topk > 0 ? batch * s_q : batch; }
 
+// Sparse units are (sequence, query token) pairs; their count is an int.
+bool units_fit(int batch, int s_q, int topk) { return topk == 0 || (long long)batch * s_q <= 0x7FFFFFFFLL; }
+
 int rows_per_unit(int s_q, int h_q, int topk) { return topk > 0 ? h_q : s_q * h_q; }
 
 // One decode workgroup per compute unit: P * row_tiles ~= #CUs, P a
@@ -150,6 +153,7 @@ MLA_EXPORT int mla_metadata_size_for_parts(int batch, int s_q, int topk, int num
                 topk, num_parts);
   if (!tile_metadata_elems || !num_splits_elems)
     return fail(MLA_ERR_INVALID_ARGUMENT, "output pointer is NULL");
+  if (!units_fit(batch, s_q, topk)) return fail(MLA_ERR_INVALID_ARGUMENT, "batch * s_q must be below 2^31");
   const int units = units_of(batch, s_q, topk);
   *tile_metadata_elems = md_elems(units, num_parts);
   *num_splits_elems = (size_t)units + 1;
@@ -185,6 +189,7 @@ MLA_EXPORT int mla_get_metadata(const int32_t* cache_seqlens, const int32_t* ind
     return fail(MLA_ERR_INVALID_ARGUMENT, "indices must be non-NULL exactly when topk > 0");
   if (!tile_metadata || !num_splits || (batch > 0 && !cache_seqlens))
     return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!units_fit(batch, s_q, topk)) return fail(MLA_ERR_INVALID_ARGUMENT, "batch * s_q must be below 2^31");
   const int units = units_of(batch, s_q, topk);
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = mla::launch_metadata(cache_seqlens, indices, s_q, topk, units, num_parts,

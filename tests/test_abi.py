@@ -59,6 +59,13 @@ def test_metadata_size_for_parts(lib):
     assert b"num_parts" in lib.mla_last_error()
     assert lib.mla_metadata_size_for_parts(1, 1, 0, 2048, ctypes.byref(md), ctypes.byref(ns)) == 0
     assert lib.mla_metadata_size_for_parts(1, 1, 0, 2049, ctypes.byref(md), ctypes.byref(ns)) == -1
+    # sparse units are (sequence, token) pairs counted in an int
+    assert lib.mla_metadata_size_for_parts(1 << 16, 1 << 15, 8, 8, ctypes.byref(md), ctypes.byref(ns)) == -1
+    assert b"2^31" in lib.mla_last_error()
+    assert lib.mla_metadata_size_for_parts(1 << 16, 1 << 15, 0, 8, ctypes.byref(md), ctypes.byref(ns)) == 0
+    fake = ctypes.c_void_p(16)   # never dereferenced: the count check fails first
+    assert lib.mla_get_metadata(fake, fake, 1 << 16, 1 << 15, 1 << 15, 1, 8, 8, fake, fake, None) == -1
+    assert b"2^31" in lib.mla_last_error()
 
 
 def _args(**kw):
