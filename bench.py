@@ -13,20 +13,23 @@ tokens, 128 heads, L = 4096, causal) is timed the same way and reported in
 bf16 TFLOPS under "mtp"; the FP8 and sparse workloads under "fp8"/"sparse".
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
-Three physical copies of each page pool (same logical cache, pages shuffled
-differently) are used in rotation so that consecutive steps do not hit the
-256 MB Infinity Cache.
+Six physical copies of each page pool (same logical cache, pages shuffled
+differently; --replicas) are used in rotation so that consecutive steps do
+not hit the 256 MB Infinity Cache.
 
-Two timed loops per workload:
+Timed loops per workload:
   * the steps replayed from HIP graphs, as a serving loop runs them: one
-    graph holds a whole rotation of consecutive steps (one per pool copy,
+    graph holds four rotations of consecutive steps (one step per pool copy,
     each step complete: schedule, split-KV kernel, combine), so the launch
-    overhead of a graph is paid once per rotation; wall time per step gives
-    `value` / `ms_per_step`.  The graphs' outputs are checked bit for bit
+    overhead of a graph is shared by 24 steps; wall time per step gives
+    `value` / `ms_per_step`.  Every graph's output is checked bit for bit
     against an eager step first.
-  * the same step launched eagerly with HIP events recorded on the launch
-    stream around each kernel; the split-KV kernel's mean event time gives
-    the roofline's `achieved` (algorithmic bytes or flops per launch over it).
+  * the split-KV kernel alone, replayed from a graph of back-to-back
+    launches (one per pool copy) with HIP events on the launch stream
+    around the replays: its mean launch duration gives the roofline's
+    `achieved` (algorithmic bytes or flops per launch over it).
+  * the same step launched eagerly with HIP events around each kernel
+    (timing_ms: per-kernel event times, which include dispatch latency).
 `roofline.traffic` (measured HBM bytes per launch) is read from the
 committed counter summary in profiles/ when it was taken on the kernel
 sources as they are now, else null.
@@ -56,6 +59,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+GRAPH_ROTATIONS = 4            # rotations of the pool copies in one graph of the timed loop
 
 
 def log(msg):
@@ -152,6 +156,16 @@ class Workload:
                     c.partial()
                     c.combine()
             self.graphs[n] = g
+        # Several rotations in one graph, so that the GPU idle time of a
+        # graph launch is shared by more steps (a serving loop's graph holds
+        # the decode step of every layer).
+        self.graph_rot = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph_rot):
+            for _ in range(GRAPH_ROTATIONS):
+                for r, c in enumerate(self.calls):
+                    m.refresh_mla_metadata(self.mds[r], self.seqlens, self.indices)
+                    c.partial()
+                    c.combine()
         # The split-KV kernel alone, once per pool copy, back to back: its
         # launch duration measured without the dispatch latency that HIP
         # events around a single eager launch include.
@@ -170,7 +184,8 @@ class Workload:
         self.step(0)
         torch.cuda.synchronize()
         ref_o, ref_l = c0.out.clone(), c0.lse.clone()
-        for n, g in self.graphs.items():
+        checks = list(self.graphs.items()) + [(GRAPH_ROTATIONS * len(self.calls), self.graph_rot)]
+        for n, g in checks:
             c0.out.fill_(0)
             c0.lse.fill_(0)
             g.replay()
@@ -180,10 +195,14 @@ class Workload:
 
     def _replay_steps(self, steps: int):
         full = len(self.calls)
-        for _ in range(steps // full):
+        big = GRAPH_ROTATIONS * full
+        for _ in range(steps // big):
+            self.graph_rot.replay()
+        rest = steps % big
+        for _ in range(rest // full):
             self.graphs[full].replay()
-        if steps % full:
-            self.graphs[steps % full].replay()
+        if rest % full:
+            self.graphs[rest % full].replay()
 
     def time_graph(self, steps: int, warmup: int) -> float:
         import torch
@@ -485,7 +504,8 @@ def main():
             "sum_seqlens": int(prim.inp.seqlens.sum()),
             "kv_bytes": kv, "kv_format": "bf16", "page_size": 64,
             "num_parts": prim.md.num_parts, "pool_replicas": args.replicas,
-            "step": f"metadata + split-KV + combine, replayed from HIP graphs of {args.replicas} consecutive steps",
+            "step": f"metadata + split-KV + combine, replayed from HIP graphs of "
+                    f"{GRAPH_ROTATIONS * args.replicas} consecutive steps",
         },
         "timing_ms": {k: round(v, 5) for k, v in tm.items()},
         # KV bytes over the decode kernels alone (split-KV + combine, HIP
