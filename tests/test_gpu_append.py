@@ -119,4 +119,4 @@ def test_decode_reads_what_append_wrote(oracle_mod, fmt):
     log(f"append then decode fmt={fmt}")
     o, l, _ = run_gpu(inp, num_parts=8)
     ro, rl = oracle_mod.decode(inp)
-    compare(o, l, ro, rl, fmt, f"append+decode fmt={fmt}")
+    compare(o, l, ro, rl, fmt, f"append+decode fmt={fmt}", inp=inp)

@@ -42,7 +42,7 @@ def test_full_size_sampled_rows(oracle_mod, name, seed):
     o, l, md = run_gpu(inp)
     sel = _sample_rows(inp, 96, seed)
     ro, rl = oracle_mod.decode(inp, sel=sel)
-    compare(o[sel], l[sel], ro, rl, inp.fmt, f"{cfg.name} ({len(sel)} rows, {md.num_parts} parts)")
+    compare(o[sel], l[sel], ro, rl, inp.fmt, f"{cfg.name} ({len(sel)} rows, {md.num_parts} parts)", inp=inp, sel=sel)
 
 
 def test_prefill_split_in_two_combines_every_row(oracle_mod):
@@ -56,7 +56,7 @@ def test_prefill_split_in_two_combines_every_row(oracle_mod):
     sel = _sample_rows(inp, 96, 907)
     sel = np.unique(np.concatenate([sel, np.arange(inp.s_q * inp.h_q - 16, inp.s_q * inp.h_q)])).astype(np.int32)
     ro, rl = oracle_mod.decode(inp, sel=sel)
-    compare(o[sel], l[sel], ro, rl, inp.fmt, f"prefill split in two ({len(sel)} rows)")
+    compare(o[sel], l[sel], ro, rl, inp.fmt, f"prefill split in two ({len(sel)} rows)", inp=inp, sel=sel)
 
 
 @pytest.mark.parametrize("num_parts", [None, 2])

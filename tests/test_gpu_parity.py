@@ -28,7 +28,7 @@ def test_tiny_workload(oracle_mod):
     inp = gen.make_inputs(gen.WORKLOADS["tiny"], poison=True)
     o, l, md = run_gpu(inp)
     ro, rl = oracle_mod.decode(inp)
-    compare(o, l, ro, rl, inp.fmt, "tiny")
+    compare(o, l, ro, rl, inp.fmt, "tiny", inp=inp)
 
 
 def _cases():
@@ -59,7 +59,28 @@ def test_random_small_shapes(oracle_mod, case):
     log(f"case b={b} s_q={s_q} h_q={h_q} L={seqlens} causal={causal} fmt={fmt} topk={topk} parts={parts}")
     o, l, _ = run_gpu(inp, num_parts=parts)
     ro, rl = oracle_mod.decode(inp)
-    compare(o, l, ro, rl, fmt, "random")
+    compare(o, l, ro, rl, fmt, "random", inp=inp)
+
+
+@pytest.mark.parametrize("h_q", [16, 64])          # 16-row tiles (R = 32) and 128-row tiles (R = 128)
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("topk", [0, 100])
+@pytest.mark.parametrize("causal", [False, True])
+def test_combination_matrix(oracle_mod, h_q, fmt, topk, causal):
+    """Every pairing of tile width, KV format, dense or sparse keys and
+    causal masking at least once, with two query tokens, lengths 0, 1, a
+    page and a bit, and a few pages, forced splits and poisoned unused slots."""
+    seed = 3000 + 8 * (h_q == 64) + 4 * fmt + 2 * (topk > 0) + int(causal)
+    cfg = gen.small_config(4, 2, h_q, [0, 1, 65, 300], causal=causal, fmt=fmt, topk=topk, seed=seed)
+    inp = gen.make_inputs(cfg, poison=True, extra_pages=2)
+    if topk:
+        rng = np.random.default_rng(seed)
+        mask = rng.random(inp.indices.shape) < 0.2
+        inp.indices[mask] = rng.integers(-5, 400, size=int(mask.sum()))
+    log(f"matrix h_q={h_q} fmt={fmt} topk={topk} causal={causal}")
+    o, l, md = run_gpu(inp, num_parts=8)
+    ro, rl = oracle_mod.decode(inp)
+    compare(o, l, ro, rl, fmt, f"matrix h_q={h_q} fmt={fmt} topk={topk} causal={causal}", inp=inp)
 
 
 @pytest.mark.parametrize("parts", [1, 7, 8, 256, 1024])
@@ -68,7 +89,7 @@ def test_num_parts_sweep(oracle_mod, parts):
     inp = gen.make_inputs(cfg, poison=True)
     o, l, _ = run_gpu(inp, num_parts=parts)
     ro, rl = oracle_mod.decode(inp)
-    compare(o, l, ro, rl, inp.fmt, f"parts={parts}")
+    compare(o, l, ro, rl, inp.fmt, f"parts={parts}", inp=inp)
 
 
 def test_schedule_matches_oracle_bitwise():
@@ -253,7 +274,7 @@ def test_sparse_prefill_shape(oracle_mod, fmt):
     for parts in (None, 24):
         o, l, _ = run_gpu(inp, num_parts=parts)
         ro, rl = oracle_mod.decode(inp)
-        compare(o, l, ro, rl, fmt, f"sparse prefill fmt={fmt} parts={parts}")
+        compare(o, l, ro, rl, fmt, f"sparse prefill fmt={fmt} parts={parts}", inp=inp)
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
@@ -271,7 +292,7 @@ def test_dense_prefill_shape(oracle_mod, fmt):
         o, l, md = run_gpu(inp, num_parts=parts)
         if parts is None:
             assert md.num_parts < 8
-        compare(o, l, ro, rl, fmt, f"dense prefill fmt={fmt} parts={md.num_parts}")
+        compare(o, l, ro, rl, fmt, f"dense prefill fmt={fmt} parts={md.num_parts}", inp=inp)
 
 
 def test_single_key_returns_v_row_bitwise():
@@ -338,7 +359,7 @@ def test_negative_scale(oracle_mod, h_q):
     inp = dataclasses.replace(inp, softmax_scale=-inp.softmax_scale)
     o, l, _ = run_gpu(inp, num_parts=8)
     ro, rl = oracle_mod.decode(inp)
-    compare(o, l, ro, rl, inp.fmt, f"negative scale h_q={h_q}")
+    compare(o, l, ro, rl, inp.fmt, f"negative scale h_q={h_q}", inp=inp)
 
 
 @pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8])
@@ -350,7 +371,7 @@ def test_wide_tiles_long_sequences(oracle_mod, fmt, parts):
     inp = gen.make_inputs(cfg, poison=True, extra_pages=2)
     o, l, _ = run_gpu(inp, num_parts=parts)
     ro, rl = oracle_mod.decode(inp)
-    compare(o, l, ro, rl, fmt, f"wide long fmt={fmt} parts={parts}")
+    compare(o, l, ro, rl, fmt, f"wide long fmt={fmt} parts={parts}", inp=inp)
 
 
 @pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8])
@@ -366,7 +387,7 @@ def test_sparse_topk_beyond_table(oracle_mod, fmt):
     for parts in (None, 5):
         o, l, _ = run_gpu(inp, num_parts=parts)
         ro, rl = oracle_mod.decode(inp)
-        compare(o, l, ro, rl, fmt, f"sparse topk=2500 fmt={fmt} parts={parts}")
+        compare(o, l, ro, rl, fmt, f"sparse topk=2500 fmt={fmt} parts={parts}", inp=inp)
 
 
 
@@ -394,7 +415,7 @@ def test_scores_growing_along_the_sequence(oracle_mod, h_q, s_q, causal):
     o, l, _ = run_gpu(inp, num_parts=8)
     ro, rl = oracle_mod.decode(inp)
     assert rl.max() - rl.min() > 100, "the test needs widely spread scores"
-    compare(o, l, ro, rl, inp.fmt, "growing scores")
+    compare(o, l, ro, rl, inp.fmt, "growing scores", inp=inp)
 
 
 @pytest.mark.parametrize("fmt", [gen.FMT_BF16, gen.FMT_FP8])
@@ -408,4 +429,4 @@ def test_narrow_pieces_longer_than_64_pages(oracle_mod, fmt, parts, s_q):
     log(f"narrow long pieces fmt={fmt} parts={parts} s_q={s_q}")
     o, l, _ = run_gpu(inp, num_parts=parts)
     ro, rl = oracle_mod.decode(inp)
-    compare(o, l, ro, rl, fmt, f"narrow long fmt={fmt} parts={parts} s_q={s_q}")
+    compare(o, l, ro, rl, fmt, f"narrow long fmt={fmt} parts={parts} s_q={s_q}", inp=inp)
