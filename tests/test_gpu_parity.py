@@ -62,7 +62,9 @@ def test_random_small_shapes(oracle_mod, case):
     compare(o, l, ro, rl, fmt, "random", inp=inp)
 
 
-@pytest.mark.parametrize("h_q", [16, 64])          # 16-row tiles (R = 32) and 128-row tiles (R = 128)
+# h_q 16: 16-row tiles (dense R = 32); 17: dense R = 34, the smallest 128-row
+# tile case, sparse R = 17, a second 16-row tile of one row; 64: 128-row tiles
+@pytest.mark.parametrize("h_q", [16, 17, 64])
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("topk", [0, 100])
 @pytest.mark.parametrize("causal", [False, True])
@@ -70,7 +72,7 @@ def test_combination_matrix(oracle_mod, h_q, fmt, topk, causal):
     """Every pairing of tile width, KV format, dense or sparse keys and
     causal masking at least once, with two query tokens, lengths 0, 1, a
     page and a bit, and a few pages, forced splits and poisoned unused slots."""
-    seed = 3000 + 8 * (h_q == 64) + 4 * fmt + 2 * (topk > 0) + int(causal)
+    seed = 3000 + 8 * (h_q == 64) + 16 * (h_q == 17) + 4 * fmt + 2 * (topk > 0) + int(causal)
     cfg = gen.small_config(4, 2, h_q, [0, 1, 65, 300], causal=causal, fmt=fmt, topk=topk, seed=seed)
     inp = gen.make_inputs(cfg, poison=True, extra_pages=2)
     if topk:
