@@ -106,12 +106,24 @@ def make_args(q, kcache, block_table, cache_seqlens, metadata: MlaMetadata, out,
     batch, s_q, h_q, d_qk = q.shape
     if block_table.dim() != 2 or block_table.shape[0] != batch:
         raise ValueError("block_table must be [batch, max_blocks]")
+    if cache_seqlens.dim() != 1 or cache_seqlens.shape[0] != batch:
+        raise ValueError("cache_seqlens must be [batch]")
     if softmax_scale is None:
         softmax_scale = d_qk ** -0.5
     topk = 0
     if indices is not None:
         _need_i32(indices, "indices")
+        if indices.dim() != 3 or tuple(indices.shape[:2]) != (batch, s_q):
+            raise ValueError("indices must be [batch, s_q, topk]")
         topk = indices.shape[2]
+    h_kv = kcache.shape[2]
+    if (metadata.batch, metadata.s_q, metadata.topk) != (batch, s_q, topk) or \
+            metadata.q_rows_per_kv_head != s_q * h_q // max(h_kv, 1):
+        raise ValueError("metadata was built for other batch / s_q / heads / topk")
+    if out.shape != (batch, s_q, h_q, int(dv)) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bf16 [{batch}, {s_q}, {h_q}, {int(dv)}] tensor")
+    if lse.shape != (batch, s_q, h_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous fp32 [{batch}, {s_q}, {h_q}] tensor")
     a = _lib.MlaDecodeArgs()
     a.batch, a.s_q, a.h_q, a.h_kv = batch, s_q, h_q, kcache.shape[2]
     a.d_qk, a.d_v, a.page_size = d_qk, int(dv), kcache.shape[1]
@@ -178,8 +190,14 @@ def refresh_mla_metadata(metadata: MlaMetadata, cache_seqlens: torch.Tensor,
     allocation), e.g. at the start of every decode step."""
     lib = _lib.load()
     _need_i32(cache_seqlens, "cache_seqlens")
-    if cache_seqlens.shape[0] != metadata.batch:
+    if cache_seqlens.dim() != 1 or cache_seqlens.shape[0] != metadata.batch:
         raise ValueError("cache_seqlens batch differs from the metadata's")
+    if (indices is None) != (metadata.topk == 0):
+        raise ValueError("indices must be given exactly when the metadata is sparse")
+    if indices is not None:
+        _need_i32(indices, "indices")
+        if tuple(indices.shape) != (metadata.batch, metadata.s_q, metadata.topk):
+            raise ValueError("indices must be [batch, s_q, topk] as when the metadata was built")
     dev = cache_seqlens.device
     with torch.cuda.device(dev):
         _lib.check(lib.mla_get_metadata(

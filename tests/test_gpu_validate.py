@@ -133,3 +133,29 @@ def test_schedule_for_another_part_count_is_named():
     call.args.num_splits = other.num_splits.data_ptr()
     call._keep = call._keep + (other,)
     _fails(call, ["24 parts"])
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The Python binding refuses, before anything is launched, tensors whose
+    shapes would make the kernels read or write outside them."""
+    from mla_paged_kv_metadata_amd import DecodeCall, get_mla_metadata, refresh_mla_metadata
+    log("binding shape checks")
+    inp, call, (q, k, bt, sl, idx, md) = _case(topk=100, s_q=2)
+    with pytest.raises(ValueError):   # out too small
+        DecodeCall(q, k, bt, sl, md, indices=idx, out=torch.empty(1, 2, 16, 512, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):   # lse of the wrong dtype
+        DecodeCall(q, k, bt, sl, md, indices=idx, lse=torch.empty(q.shape[:3], dtype=torch.float64, device="cuda"))
+    with pytest.raises(ValueError):   # indices with a smaller top-k than the metadata's
+        DecodeCall(q, k, bt, sl, md, indices=idx[:, :, :50].contiguous())
+    with pytest.raises(ValueError):
+        refresh_mla_metadata(md, sl, idx[:, :, :50].contiguous())
+    with pytest.raises(ValueError):   # dense call on sparse metadata
+        refresh_mla_metadata(md, sl, None)
+    with pytest.raises(ValueError):   # metadata for other heads
+        md8 = get_mla_metadata(sl, 2 * 8, 1, s_q=2, indices=idx)
+        DecodeCall(q, k, bt, sl, md8, indices=idx)
+    with pytest.raises(ValueError):   # cache_seqlens of another batch
+        DecodeCall(q, k, bt, sl[:3].contiguous(), md, indices=idx)
+    out, lse = call.run()             # the well-formed call still runs
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
