@@ -11,7 +11,8 @@ from gpu_util import log, to_device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("h_q,fmt,topk", [(16, 0, 0), (128, 0, 0), (16, 1, 0), (128, 1, 100)])
+@pytest.mark.parametrize("h_q,fmt,topk", [(16, 0, 0), (128, 0, 0), (16, 1, 0), (128, 1, 100),
+                                          (16, 0, 200), (128, 1, 0), (128, 0, 100)])
 def test_graph_replay_matches_eager(h_q, fmt, topk):
     from mla_paged_kv_metadata_amd import DecodeCall, get_mla_metadata, refresh_mla_metadata
     seqlens = [700, 1, 333, 0, 2048, 129]
