@@ -289,17 +289,20 @@ __global__ __launch_bounds__(kMdThreads) void metadata_kernel(const int32_t* __r
     for (int i = tid; i < kDoneBits / 32; i += kMdThreads) done[i] = 0u;
     __syncthreads();
     // A row whose last entry points into the sequence spans all its blocks
-    // (the usual case): one thread per unit reads just that entry.
+    // (the usual case): one thread per unit reads just that entry.  Only
+    // units that have a done bit are settled here; the scan below counts
+    // every other unit (units from kDoneBits on are always scanned).
     const int n_all = (topk + kPage - 1) / kPage;
     for (int u = tid; u < units; u += kMdThreads) {
-      const int last = indices[(size_t)u * topk + topk - 1];
       const int Lu = seqlens[u / s_q];
       if (u < kUnitCache) ulen[u] = Lu;
+      if (u >= kDoneBits) continue;
+      const int last = indices[(size_t)u * topk + topk - 1];
       if (last >= 0 && last < Lu) {
         unit_blocks[u] = n_all;
         if (u < kUnitCache) ucnt[u] = n_all;
         cost += n_all + c0;
-        if (u < kDoneBits) atomicOr(&done[u >> 5], 1u << (u & 31));
+        atomicOr(&done[u >> 5], 1u << (u & 31));
       }
     }
     __syncthreads();

@@ -126,7 +126,7 @@ def test_schedule_matches_oracle_bitwise():
 
 @pytest.mark.parametrize("units,sparse", [(1, True), (63, True), (64, True), (65, True), (4096, True),
                                           (4097, True), (65, False), (4096, False), (4097, False),
-                                          (6000, False)])
+                                          (6000, False), (70000, True)])
 def test_schedule_unit_count_boundaries(units, sparse):
     """Unit counts on both sides of the schedule kernel's switches: at most
     64 sparse units read in one pass, and the first 4096 units' counts and
@@ -139,11 +139,13 @@ def test_schedule_unit_count_boundaries(units, sparse):
     s_q = 1
     if sparse:
         s_q = 3 if units % 3 == 0 else 1
+        if units > 65536:   # past the done bits of the one-entry pass: one sequence, many query tokens
+            s_q = units
     b = units // s_q
     sl = rng.integers(0, 9000, size=b).astype(np.int32)
     idx = None
     if sparse:
-        topk = 520 if units <= 65 else 132
+        topk = 520 if units <= 65 else (132 if units <= 65536 else 72)
         ind = rng.integers(0, 9000, size=(b, s_q, topk)).astype(np.int32) % np.maximum(sl, 1)[:, None, None]
         cut = rng.integers(0, topk + 1, size=(b, s_q))
         for i in range(b):
@@ -306,20 +308,71 @@ def test_single_key_returns_v_row_bitwise():
         assert np.array_equal(o.reshape(3, 16, 512)[b], np.broadcast_to(v.astype(np.float64), (16, 512)))
 
 
-def test_zero_query_counts_keys():
-    seqlens = [1, 63, 64, 65, 127, 128, 129, 1000, 4097]
-    cfg = gen.small_config(len(seqlens), 2, 16, seqlens, causal=True, seed=42)
+def _visible_v(inp, b, keys):
+    """V rows (fp64) of logical keys `keys` of sequence b, through the block
+    table (bf16 pool)."""
+    keys = np.asarray(keys, dtype=np.int64)
+    pages = inp.block_table[b, keys >> 6].astype(np.int64)
+    rows = inp.kcache.reshape(-1, 576)[pages * 64 + (keys & 63)]
+    return gen.bf16_bits_to_f32(rows[:, :512]).astype(np.float64)
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_zero_query_counts_keys(h_q):
+    """q = 0: every score is 0, so lse = ln N exactly for N visible keys
+    (1e-5 separates N from N + 1 up to 32K keys) and out = the plain mean of
+    the visible V rows.  Causal s_q = 2 sees L - 1, then L keys; the lengths
+    cover every tail residue mod 64 (and several pages), on both tile
+    kernels, with forced splits."""
+    seqlens = [64 * (r % 5) + r for r in range(64)] + [1000, 4097]
+    cfg = gen.small_config(len(seqlens), 2, h_q, seqlens, causal=True, seed=42)
     inp = gen.make_inputs(cfg, poison=True)
     inp.q[:] = 0
+    log(f"zero query h_q={h_q}")
     o, l, _ = run_gpu(inp, num_parts=16)
-    l = l.reshape(len(seqlens), 2, 16)
+    l = l.reshape(len(seqlens), 2, h_q)
+    o = o.reshape(len(seqlens), 2, h_q, 512)
     for b, L in enumerate(seqlens):
         for s in range(2):
             n = L - 1 + s
-            if n == 0:
-                assert np.all(np.isneginf(l[b, s]))
-            else:
-                assert np.all(np.abs(l[b, s] - np.log(n)) <= 1e-5), (b, s, l[b, s, 0], np.log(n))
+            if n <= 0:
+                assert np.all(np.isneginf(l[b, s])) and np.all(o[b, s] == 0)
+                continue
+            assert np.all(np.abs(l[b, s] - np.log(n)) <= 1e-5), (b, s, l[b, s, 0], np.log(n))
+            mean = _visible_v(inp, b, np.arange(n)).mean(axis=0)
+            assert np.all(np.abs(o[b, s] - mean[None, :]) <= 2e-3 + 2.0 ** -7 * np.abs(mean)[None, :]), (b, s)
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_zero_query_sparse_counts_valid_entries(h_q):
+    """Sparse q = 0 with -1 tails and out-of-range entries: lse = ln(number of
+    entries inside [0, L)), out = the mean of their V rows (repeated entries
+    counted again)."""
+    seqlens = [300, 1, 64, 129, 0]
+    topk = 150
+    rng = np.random.default_rng(9)
+    cfg = gen.small_config(len(seqlens), 1, h_q, seqlens, topk=topk, seed=48)
+    inp = gen.make_inputs(cfg, poison=True)
+    inp.q[:] = 0
+    idx = rng.integers(-3, 400, size=(len(seqlens), 1, topk)).astype(np.int32)
+    idx[0, 0, 100:] = -1                 # a -1 tail
+    idx[1, 0, :] = -1
+    idx[1, 0, 7] = 0                     # the only key of a 1-token sequence
+    idx[2, 0, :64] = np.arange(64)
+    idx[2, 0, 64:] = 5                   # key 5 repeated
+    inp.indices = idx
+    log(f"zero query sparse h_q={h_q}")
+    o, l, _ = run_gpu(inp, num_parts=16)
+    l = l.reshape(len(seqlens), h_q)
+    o = o.reshape(len(seqlens), h_q, 512)
+    for b, L in enumerate(seqlens):
+        keys = idx[b, 0][(idx[b, 0] >= 0) & (idx[b, 0] < L)]
+        if keys.size == 0:
+            assert np.all(np.isneginf(l[b])) and np.all(o[b] == 0)
+            continue
+        assert np.all(np.abs(l[b] - np.log(keys.size)) <= 1e-5), (b, keys.size, l[b, 0])
+        mean = _visible_v(inp, b, keys).mean(axis=0)
+        assert np.all(np.abs(o[b] - mean[None, :]) <= 2e-3 + 2.0 ** -7 * np.abs(mean)[None, :]), b
 
 
 def test_page_permutation_bitwise():
