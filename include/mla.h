@@ -96,20 +96,29 @@ typedef struct {
  * Sizes of the schedule arrays (topnet.top "Was ist FlashMLA?",
  * "MLA-Metadaten abrufen": get_mla_metadata(cache_seqlens,
  * s_q * h_q // h_kv, h_kv) returns tile_scheduler_metadata and num_splits).
+ * The pages pass no s_q and return no part count; here the caller passes
+ * s_q (sparse schedules have one unit per query token) and gets back the
+ * part count, which every later call of the step takes.
  *
  *   q_rows_per_kv_head = s_q * h_q / h_kv; topk = 0 for dense.
  *   *num_parts (out): the part count the library picks for this device and
- *                     row count (a multiple of 8).
+ *     row count: about (compute units) / (row tiles of one unit) parts,
+ *     rounded down to a multiple of 8 when that leaves at least 8 (whole
+ *     XCD groups), otherwise 1..7 (the row tiles alone nearly fill the
+ *     device, e.g. a prefill).
  *   *tile_metadata_elems, *num_splits_elems (out): int32 element counts to
  *     allocate, for the picked part count.  Use
  *     mla_metadata_size_for_parts to size for a forced count.
+ * Errors: MLA_ERR_UNSUPPORTED for h_kv != 1; MLA_ERR_INVALID_ARGUMENT for a
+ * bad count or a NULL output; MLA_ERR_HIP if the device cannot be queried.
  */
-int mla_metadata_size(int batch, int s_q, int q_rows_per_kv_head, int h_kv, int topk,
-                      int *num_parts, size_t *tile_metadata_elems, size_t *num_splits_elems);
+mla_status mla_metadata_size(int batch, int s_q, int q_rows_per_kv_head, int h_kv, int topk,
+                             int *num_parts, size_t *tile_metadata_elems, size_t *num_splits_elems);
 
-/* Same sizes for an explicit part count (1 <= num_parts <= 2048). */
-int mla_metadata_size_for_parts(int batch, int s_q, int topk, int num_parts,
-                                size_t *tile_metadata_elems, size_t *num_splits_elems);
+/* Same sizes for an explicit part count (1 <= num_parts <= 2048); same
+ * passage.  Host only, launches nothing. */
+mla_status mla_metadata_size_for_parts(int batch, int s_q, int topk, int num_parts,
+                                       size_t *tile_metadata_elems, size_t *num_splits_elems);
 
 /*
  * Build the split-KV schedule on the device (same passage as above).
@@ -132,14 +141,23 @@ int mla_metadata_size_for_parts(int batch, int s_q, int topk, int num_parts,
  * The result depends only on cache_seqlens (and indices); compute it once
  * per decode step and reuse it for every layer.
  */
-int mla_get_metadata(const int32_t *cache_seqlens, const int32_t *indices, int batch, int s_q,
-                     int q_rows_per_kv_head, int h_kv, int topk, int num_parts,
-                     int32_t *tile_metadata, int32_t *num_splits, void *stream);
+mla_status mla_get_metadata(const int32_t *cache_seqlens, const int32_t *indices, int batch, int s_q,
+                            int q_rows_per_kv_head, int h_kv, int topk, int num_parts,
+                            int32_t *tile_metadata, int32_t *num_splits, void *stream);
 
-/* Bytes of device workspace mla_decode_kvcache needs for these arguments
- * (bf16 partial outputs, each normalised by its own row sum, and fp32
- * partial log-sum-exps of split sequences). */
-int mla_workspace_size(const mla_decode_args *args, size_t *bytes);
+/* Bytes of device workspace mla_decode_kvcache needs for these arguments:
+ * the partial results of sequences whose keys the schedule splits over
+ * several parts (topnet.top "Was ist FlashMLA?", "MLA-Metadaten abrufen":
+ * num_splits counts those pieces per sequence), as bf16 partial outputs,
+ * each normalised by its own row sum, and fp32 partial log-sum-exps.  The
+ * contents need no initialisation.  Host only; errors as for the decode's
+ * shape checks (the pointers in args are not read).
+ * Layout, with R query rows per unit (s_q * h_q dense, h_q sparse) and
+ * slots = units + num_parts: partial outputs [slots, R, 512] bf16 at byte 0,
+ * then partial log-sum-exps [slots, R] fp32 at byte
+ * align256(slots * R * 1024); piece i of unit u (0 <= i < num_splits[u+1] -
+ * num_splits[u]) is slot num_splits[u] + i. */
+mla_status mla_workspace_size(const mla_decode_args *args, size_t *bytes);
 
 /*
  * Decode one layer: out and lse for every (sequence, query token, head)
@@ -150,16 +168,22 @@ int mla_workspace_size(const mla_decode_args *args, size_t *bytes);
  *
  * Enqueues the split-KV attention kernel and the log-sum-exp combine kernel
  * on `stream`.  The metadata must come from mla_get_metadata with the same
- * batch, s_q, h_q * s_q, topk, cache_seqlens, indices and num_parts.
+ * batch, s_q, h_q * s_q, topk, cache_seqlens, indices and num_parts.  The
+ * kernels check the schedule's header on the device: if it was built for
+ * another part or unit count (or is not a schedule), no key is read and
+ * every row gets out = 0 and lse = NaN (the call itself cannot see this
+ * and returns MLA_OK; mla_validate_inputs names the problem).
  * Limits (MLA_ERR_INVALID_ARGUMENT beyond them): batch * s_q * h_q below
  * 2^31 query rows, and num_parts (rounded up to a multiple of 8 when >= 8)
  * times the row tiles of one unit below 2^31 workgroups.
  */
-int mla_decode_kvcache(const mla_decode_args *args, void *stream);
+mla_status mla_decode_kvcache(const mla_decode_args *args, void *stream);
 
 /*
- * The two halves of mla_decode_kvcache, for callers that schedule them
- * separately (e.g. to time each kernel, or to overlap the combine with
+ * The two halves of mla_decode_kvcache (same passages: the per-layer decode
+ * of topnet.top "Was ist FlashMLA?", "MLA-Decodierung ausfuehren", and the
+ * merge of the num_splits pieces of "MLA-Metadaten abrufen"), for callers
+ * that schedule them separately (e.g. to time each kernel, or to overlap the combine with
  * other work).  mla_decode_partial enqueues only the split-KV attention
  * kernel: sequences covered by one part get their final out/lse, split
  * sequences leave partial results in the workspace.  mla_decode_combine
@@ -169,8 +193,8 @@ int mla_decode_kvcache(const mla_decode_args *args, void *stream);
  * enqueued); it must follow mla_decode_partial on the same arguments and
  * workspace.  Same arguments and errors as mla_decode_kvcache.
  */
-int mla_decode_partial(const mla_decode_args *args, void *stream);
-int mla_decode_combine(const mla_decode_args *args, void *stream);
+mla_status mla_decode_partial(const mla_decode_args *args, void *stream);
+mla_status mla_decode_combine(const mla_decode_args *args, void *stream);
 
 /*
  * Debug audit of the values a decode call reads from device memory, which
@@ -193,7 +217,22 @@ int mla_decode_combine(const mla_decode_args *args, void *stream);
  * MLA_ERR_INVALID_ARGUMENT with mla_last_error() naming the first problem
  * (MLA_ERR_HIP if a copy or the wait fails).  Not capturable in a graph.
  */
-int mla_validate_inputs(const mla_decode_args *args, void *stream);
+mla_status mla_validate_inputs(const mla_decode_args *args, void *stream);
+
+/*
+ * The same audit (same passage) on copies the caller already holds in HOST
+ * memory: cache_seqlens [batch], block_table [batch * max_blocks_per_seq],
+ * indices [batch * s_q * topk] (ignored when topk = 0), tile_metadata (the
+ * element count mla_metadata_size_for_parts gives for args->num_parts; only
+ * its 8-int header is read when the header names other part or unit
+ * counts) and num_splits [units + 1].  The device pointers in args are not
+ * read; the shape checks of the decode apply.  Synchronous, touches no
+ * device.  Returns MLA_OK or MLA_ERR_INVALID_ARGUMENT naming the first
+ * problem.
+ */
+mla_status mla_validate_host_inputs(const mla_decode_args *args, const int32_t *cache_seqlens,
+                                    const int32_t *block_table, const int32_t *indices,
+                                    const int32_t *tile_metadata, const int32_t *num_splits);
 
 /*
  * Write new tokens' latent rows into the page pool: the cache update that
@@ -218,8 +257,8 @@ int mla_validate_inputs(const mla_decode_args *args, void *stream);
  * Enqueued on `stream`; n = 0 is a no-op.  The pool rows of other slots are
  * not touched.
  */
-int mla_append_kv(const void *rows, const int32_t *slots, int n, int kv_format, void *kcache,
-                  int num_pages, void *stream);
+mla_status mla_append_kv(const void *rows, const int32_t *slots, int n, int kv_format, void *kcache,
+                         int num_pages, void *stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *mla_last_error(void);

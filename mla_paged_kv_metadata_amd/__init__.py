@@ -1,8 +1,8 @@
 """MI355X-native MLA decoding over a 64-token paged KV cache.
 
     md = get_mla_metadata(cache_seqlens, s_q * h_q // h_kv, h_kv)   # once per step
-    out, lse = mla_decode_kvcache(q, kcache, block_table, cache_seqlens, md,
-                                  causal=..., indices=...)         # per layer
+    out, lse = mla_decode_kvcache(q, kcache, block_table, cache_seqlens,
+                                  causal=..., indices=..., metadata=md)   # per layer
 
 The work runs in hand-written gfx950 HIP kernels in libmla.so (C ABI in
 include/mla.h); this package only marshals torch tensors into that ABI.

@@ -155,15 +155,22 @@ def workspace_bytes(args: _lib.MlaDecodeArgs) -> int:
 
 
 def mla_decode_kvcache(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tensor,
-                       cache_seqlens: torch.Tensor, metadata: MlaMetadata,
-                       softmax_scale: Optional[float] = None, causal: bool = False,
-                       indices: Optional[torch.Tensor] = None, dv: int = D_V,
+                       cache_seqlens: torch.Tensor, softmax_scale: Optional[float] = None,
+                       causal: bool = False, indices: Optional[torch.Tensor] = None,
+                       metadata: Optional[MlaMetadata] = None, dv: int = D_V,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None):
-    """Decode one layer; returns (out [b, s_q, h_q, 512] bf16, lse [b, s_q, h_q] fp32)."""
+    """Decode one layer; returns (out [b, s_q, h_q, 512] bf16, lse [b, s_q, h_q] fp32).
+
+    `metadata` is the step's schedule from get_mla_metadata, built once per
+    decode step and passed to every layer; when it is omitted the schedule
+    is built here on the same stream (one more kernel launch)."""
     lib = _lib.load()
     batch, s_q, h_q, _ = q.shape
     dev = q.device
+    if metadata is None:
+        metadata = get_mla_metadata(cache_seqlens, s_q * h_q // max(kcache.shape[2], 1), kcache.shape[2],
+                                    s_q=s_q, indices=indices)
     if out is None:
         out = torch.empty(batch, s_q, h_q, dv, dtype=torch.bfloat16, device=dev)
     if lse is None:

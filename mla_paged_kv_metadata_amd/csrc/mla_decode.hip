@@ -38,11 +38,16 @@ __device__ __forceinline__ void acc_bf16x8(f32x4& a0, f32x4& a1, float w, const 
   a1[3] += w * __builtin_bit_cast(float, v[3] & 0xFFFF0000u);
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ num_splits,
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ md,
+                                                      const int32_t* __restrict__ num_splits,
                                                       const uint16_t* __restrict__ ws_o,
                                                       const float* __restrict__ ws_lse,
                                                       uint16_t* __restrict__ out,
-                                                      float* __restrict__ lse, int R) {
+                                                      float* __restrict__ lse, int R, int num_parts,
+                                                      int units) {
+  // A schedule that does not match the call: the split-KV kernel has
+  // already given every row out = 0 and lse = NaN; nothing to merge.
+  if (md[0] != num_parts || md[5] != kMagic || md[3] != units) return;
   // Workgroup = (unit, four rows), flattened so that any row count fits.
   const int quads = (R + 3) / 4;
   const int u = blockIdx.x / quads;
@@ -112,8 +117,8 @@ hipError_t launch_decode(const DecodeParams& p, int kv_format, int which, hipStr
   // With a single part no unit is split: there is nothing to combine.
   if ((which & 2) && p.num_parts > 1) {
     const dim3 cgrid((unsigned)((size_t)p.units * ((p.R + 3) / 4)));
-    hipLaunchKernelGGL(combine_kernel, cgrid, dim3(256), 0, stream, p.num_splits, p.ws_o, p.ws_lse,
-                       p.out, p.lse, p.R);
+    hipLaunchKernelGGL(combine_kernel, cgrid, dim3(256), 0, stream, p.md, p.num_splits, p.ws_o, p.ws_lse,
+                       p.out, p.lse, p.R, p.num_parts, p.units);
     return hipGetLastError();
   }
   return hipSuccess;

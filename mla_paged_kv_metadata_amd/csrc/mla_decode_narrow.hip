@@ -119,12 +119,16 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
   // row tiles of one part share an XCD and its L2).
   int part, rt;
   work_item(blockIdx.x, p.num_parts, p.row_tiles, &part, &rt);
-  if (part >= p.num_parts) return;
-  // Header and part row are read together (one round trip).
-  const int32_t* prow = p.md + kHeader + kPartRow * part;
+  // Header and part row are read together (one round trip); workgroups
+  // past the last part read the last part's row and then stop.
+  const int32_t* prow = p.md + kHeader + kPartRow * min(part, p.num_parts - 1);
   const int h0 = p.md[0], h3 = p.md[3], h5 = p.md[5];
   const int u0 = prow[0], j0 = prow[1], u1 = prow[2], j1 = prow[3], split0 = prow[4];
-  if (h0 != p.num_parts || h5 != kMagic || h3 != p.units || u0 < 0) return;
+  if (!header_ok(p, h0, h3, h5)) {
+    fill_mismatch<kThreads>(p);
+    return;
+  }
+  if (part >= p.num_parts || u0 < 0) return;
   const int32_t* unit_blocks = p.md + kHeader + kPartRow * p.num_parts;
 
   const int row_base = rt * kRows;   // uniform

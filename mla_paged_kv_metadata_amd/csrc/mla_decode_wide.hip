@@ -413,10 +413,15 @@ struct Item {
   int part, rt, u0, j0, u1, j1, split0;
   const int32_t* unit_blocks;
 };
+// A schedule header that does not match the call gives every row out = 0
+// and lse = NaN (fill_mismatch) and no work item.
 __device__ __forceinline__ bool decode_item(const DecodeParams& p, Item& it) {
   work_item(blockIdx.x, p.num_parts, p.row_tiles, &it.part, &it.rt);
+  if (!header_ok(p, p.md[0], p.md[3], p.md[5])) {
+    fill_mismatch<kThreads>(p);
+    return false;
+  }
   if (it.part >= p.num_parts) return false;
-  if (p.md[0] != p.num_parts || p.md[5] != kMagic || p.md[3] != p.units) return false;
   const int32_t* prow = p.md + kHeader + kPartRow * it.part;
   it.u0 = prow[0];
   it.j0 = prow[1];

@@ -199,6 +199,28 @@ __device__ __forceinline__ void dequant_slice(const uint8_t* raw, uint8_t* dst) 
   }
 }
 
+// The schedule's header does not match the call (built for another part or
+// unit count, or not by the schedule kernel): nothing in it can be trusted,
+// so no key is read.  Every workgroup of the grid writes out = 0 and
+// lse = NaN for its share of all query rows (one row per wave at a time,
+// strided by the grid), so that no row keeps stale memory.
+template <int THREADS>
+__device__ __forceinline__ void fill_mismatch(const DecodeParams& p) {
+  constexpr int kW = THREADS / 64;
+  const int lane = threadIdx.x & 63;
+  const long long total = (long long)p.units * p.R;
+  for (long long r = (long long)blockIdx.x * kW + (threadIdx.x >> 6); r < total;
+       r += (long long)gridDim.x * kW) {
+    *(u32x4*)(p.out + r * kDv + 8 * lane) = u32x4{0u, 0u, 0u, 0u};
+    if (lane == 0) p.lse[r] = __builtin_nanf("");
+  }
+}
+
+// True when the header of the schedule matches the call.
+__device__ __forceinline__ bool header_ok(const DecodeParams& p, int h0, int h3, int h5) {
+  return h0 == p.num_parts && h5 == kMagic && h3 == p.units;
+}
+
 template <int C>
 struct Slot {
   static constexpr int value = C;

@@ -114,7 +114,7 @@ def run_gpu(inp: gen.Inputs, num_parts=None, dev_tensors=None):
     from mla_paged_kv_metadata_amd import get_mla_metadata, mla_decode_kvcache
     q, k, bt, sl, idx = dev_tensors if dev_tensors is not None else to_device(inp)
     md = get_mla_metadata(sl, inp.s_q * inp.h_q, 1, s_q=inp.s_q, indices=idx, num_parts=num_parts)
-    out, lse = mla_decode_kvcache(q, k, bt, sl, md, softmax_scale=inp.softmax_scale,
+    out, lse = mla_decode_kvcache(q, k, bt, sl, metadata=md, softmax_scale=inp.softmax_scale,
                                   causal=inp.causal, indices=idx)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy().astype(np.float64).reshape(-1, 512)

@@ -83,7 +83,7 @@ def test_long_prefill_past_32_bit_byte_offsets(oracle_mod, num_parts):
     from mla_paged_kv_metadata_amd import get_mla_metadata, mla_decode_kvcache
     log(f"long prefill s_q={s_q} h_q={h_q} L={L} num_parts={num_parts}")
     md = get_mla_metadata(sl, s_q * h_q, 1, s_q=s_q, num_parts=num_parts)
-    out, lse = mla_decode_kvcache(q, k, bt, sl, md, softmax_scale=kv.softmax_scale, causal=True)
+    out, lse = mla_decode_kvcache(q, k, bt, sl, softmax_scale=kv.softmax_scale, causal=True, metadata=md)
     torch.cuda.synchronize()
     if num_parts == 2:
         assert int(md.num_splits[-1]) == 2

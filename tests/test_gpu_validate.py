@@ -159,3 +159,39 @@ def test_binding_rejects_mismatched_shapes():
     out, lse = call.run()             # the well-formed call still runs
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("h_q,topk,fmt", [(16, 0, 0), (128, 0, 0), (128, 64, 1), (16, 64, 1)])
+def test_schedule_header_mismatch_gives_defined_output(h_q, topk, fmt):
+    """A decode whose num_parts differs from the schedule's, or whose
+    schedule header is not one, reads no key: every row gets out = 0 and
+    lse = NaN instead of whatever the buffers held."""
+    import ctypes
+    from mla_paged_kv_metadata_amd import DecodeCall, get_mla_metadata, _lib
+    log(f"header mismatch h_q={h_q} topk={topk} fmt={fmt}")
+    seqlens = [700, 1, 333, 0, 2048, 129]
+    cfg = gen.small_config(len(seqlens), 1, h_q, seqlens, fmt=fmt, topk=topk, seed=5, max_blocks=40)
+    inp = gen.make_inputs(cfg, extra_pages=2)
+    q, k, bt, sl, idx = to_device(inp)
+    md = get_mla_metadata(sl, h_q, 1, s_q=1, indices=idx, num_parts=16)
+    call = DecodeCall(q, k, bt, sl, md, indices=idx)
+    lib = _lib.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for how in ("num_parts", "magic"):
+        call.out.fill_(7.0)
+        call.lse.fill_(3.0)
+        if how == "num_parts":
+            call.args.num_parts = 8      # the schedule holds 16 parts
+        else:
+            call.args.num_parts = 16
+            md.tile_metadata[5] = 0      # not a schedule header
+        _lib.check(lib.mla_decode_kvcache(ctypes.byref(call.args), stream))
+        torch.cuda.synchronize()
+        assert torch.isnan(call.lse).all(), how
+        assert (call.out == 0).all(), how
+    # a fresh schedule decodes normally again
+    md2 = get_mla_metadata(sl, h_q, 1, s_q=1, indices=idx, num_parts=16)
+    call2 = DecodeCall(q, k, bt, sl, md2, indices=idx)
+    o, l = call2.run()
+    torch.cuda.synchronize()
+    assert not torch.isnan(l).any()
