@@ -9,7 +9,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla.so")
+# MLA_LIB_PATH selects another build of the same library (the sanitizer
+# test loads a host-instrumented copy that way).
+LIB_PATH = os.environ.get("MLA_LIB_PATH") or os.path.join(_HERE, "libmla.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARGUMENT = -1
@@ -29,6 +31,7 @@ EXPORTED = (
     "mla_decode_partial",
     "mla_decode_combine",
     "mla_validate_inputs",
+    "mla_validate_host_inputs",
     "mla_append_kv",
     "mla_last_error",
     "mla_version",
@@ -92,13 +95,15 @@ def load() -> ctypes.CDLL:
     lib.mla_decode_partial.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
     lib.mla_decode_combine.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
     lib.mla_validate_inputs.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
+    lib.mla_validate_host_inputs.argtypes = [ctypes.POINTER(MlaDecodeArgs), P, P, P, P, P]
     lib.mla_append_kv.argtypes = [P, P, i, i, P, i, P]
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
     lib.mla_version.argtypes = []
     for name in ("mla_metadata_size", "mla_metadata_size_for_parts", "mla_get_metadata",
                  "mla_workspace_size", "mla_decode_kvcache", "mla_decode_partial",
-                 "mla_decode_combine", "mla_validate_inputs", "mla_append_kv", "mla_version"):
+                 "mla_decode_combine", "mla_validate_inputs", "mla_validate_host_inputs",
+                 "mla_append_kv", "mla_version"):
         getattr(lib, name).restype = i
     _lib = lib
     return lib

@@ -39,8 +39,8 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, objdir: str = BUILD) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [_hipcc(), *COMMON, *extra, "-c", *lang, os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,21 +49,22 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra=None, verbose: bool = False) -> str:
-    """Compile every HIP source and link libmla.so; returns its path."""
+def build(extra=None, verbose: bool = False, out: str = LIB, objdir: str = BUILD, link_extra=None) -> str:
+    """Compile every HIP source and link libmla.so (or `out`, with objects in
+    `objdir`); returns its path."""
     extra = list(extra or [])
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(objdir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, extra, objdir), SOURCES))
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *(link_extra or []), *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -20,7 +20,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int status, const char* fmt, ...) {
+mla_status fail(mla_status status, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -30,7 +30,7 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
-int ok() {
+mla_status ok() {
   g_last_error.clear();
   return MLA_OK;
 }
@@ -40,7 +40,7 @@ std::mutex g_cu_mutex;
 int g_cu_count[kMaxDevices] = {0};
 
 // Compute units of the current device (cached per device).
-int current_cu_count(int* cus) {
+mla_status current_cu_count(int* cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice failed");
   if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_HIP, "device id %d out of range", dev);
@@ -91,7 +91,7 @@ void workspace_layout(int units, int parts, int R, size_t* o_bytes, size_t* tota
 }
 
 // Shape and option checks (no pointers): enough for workspace sizing.
-int check_decode_shape(const mla_decode_args* a) {
+mla_status check_decode_shape(const mla_decode_args* a) {
   if (!a) return fail(MLA_ERR_INVALID_ARGUMENT, "args is NULL");
   if (a->h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv must be 1 (got %d)", a->h_kv);
   if (a->d_qk != mla::kDqk || a->d_v != mla::kDv)
@@ -128,8 +128,8 @@ int check_decode_shape(const mla_decode_args* a) {
   return MLA_OK;
 }
 
-int check_decode_args(const mla_decode_args* a) {
-  int st = check_decode_shape(a);
+mla_status check_decode_args(const mla_decode_args* a) {
+  mla_status st = check_decode_shape(a);
   if (st != MLA_OK) return st;
   if (a->topk > 0 && !a->indices) return fail(MLA_ERR_INVALID_ARGUMENT, "indices is NULL");
   if (a->batch > 0) {
@@ -146,7 +146,7 @@ MLA_EXPORT int mla_version(void) { return 1; }
 
 MLA_EXPORT const char* mla_last_error(void) { return g_last_error.c_str(); }
 
-MLA_EXPORT int mla_metadata_size_for_parts(int batch, int s_q, int topk, int num_parts,
+MLA_EXPORT mla_status mla_metadata_size_for_parts(int batch, int s_q, int topk, int num_parts,
                                            size_t* tile_metadata_elems, size_t* num_splits_elems) {
   if (batch < 0 || s_q < 1 || topk < 0 || num_parts < 1 || num_parts > mla::kMaxParts)
     return fail(MLA_ERR_INVALID_ARGUMENT, "bad batch/s_q/topk/num_parts (%d/%d/%d/%d)", batch, s_q,
@@ -160,7 +160,7 @@ MLA_EXPORT int mla_metadata_size_for_parts(int batch, int s_q, int topk, int num
   return ok();
 }
 
-MLA_EXPORT int mla_metadata_size(int batch, int s_q, int q_rows_per_kv_head, int h_kv, int topk,
+MLA_EXPORT mla_status mla_metadata_size(int batch, int s_q, int q_rows_per_kv_head, int h_kv, int topk,
                                  int* num_parts, size_t* tile_metadata_elems,
                                  size_t* num_splits_elems) {
   if (h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv must be 1 (got %d)", h_kv);
@@ -170,7 +170,7 @@ MLA_EXPORT int mla_metadata_size(int batch, int s_q, int q_rows_per_kv_head, int
                 q_rows_per_kv_head, s_q);
   if (!num_parts) return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts is NULL");
   int cus = 0;
-  int st = current_cu_count(&cus);
+  mla_status st = current_cu_count(&cus);
   if (st != MLA_OK) return st;
   const int h_q = q_rows_per_kv_head / s_q;
   *num_parts = auto_parts(rows_per_unit(s_q, h_q, topk), cus);
@@ -178,7 +178,7 @@ MLA_EXPORT int mla_metadata_size(int batch, int s_q, int q_rows_per_kv_head, int
                                      num_splits_elems);
 }
 
-MLA_EXPORT int mla_get_metadata(const int32_t* cache_seqlens, const int32_t* indices, int batch,
+MLA_EXPORT mla_status mla_get_metadata(const int32_t* cache_seqlens, const int32_t* indices, int batch,
                                 int s_q, int q_rows_per_kv_head, int h_kv, int topk, int num_parts,
                                 int32_t* tile_metadata, int32_t* num_splits, void* stream) {
   if (h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv must be 1 (got %d)", h_kv);
@@ -198,8 +198,8 @@ MLA_EXPORT int mla_get_metadata(const int32_t* cache_seqlens, const int32_t* ind
   return ok();
 }
 
-MLA_EXPORT int mla_workspace_size(const mla_decode_args* args, size_t* bytes) {
-  int st = check_decode_shape(args);
+MLA_EXPORT mla_status mla_workspace_size(const mla_decode_args* args, size_t* bytes) {
+  mla_status st = check_decode_shape(args);
   if (st != MLA_OK) return st;
   if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
   size_t ob;
@@ -211,7 +211,7 @@ MLA_EXPORT int mla_workspace_size(const mla_decode_args* args, size_t* bytes) {
 namespace {
 
 // Workspace present and large enough; *o_bytes = offset of the partial lse.
-int check_workspace(const mla_decode_args* a, size_t* o_bytes) {
+mla_status check_workspace(const mla_decode_args* a, size_t* o_bytes) {
   size_t need;
   workspace_layout(units_of(a->batch, a->s_q, a->topk), a->num_parts,
                    rows_per_unit(a->s_q, a->h_q, a->topk), o_bytes, &need);
@@ -221,8 +221,8 @@ int check_workspace(const mla_decode_args* a, size_t* o_bytes) {
   return MLA_OK;
 }
 
-int decode_impl(const mla_decode_args* a, void* stream, int which) {
-  int st = check_decode_args(a);
+mla_status decode_impl(const mla_decode_args* a, void* stream, int which) {
+  mla_status st = check_decode_args(a);
   if (st != MLA_OK) return st;
   if (a->batch == 0) return ok();
   const int units = units_of(a->batch, a->s_q, a->topk);
@@ -262,22 +262,22 @@ int decode_impl(const mla_decode_args* a, void* stream, int which) {
 
 }  // namespace
 
-MLA_EXPORT int mla_decode_kvcache(const mla_decode_args* a, void* stream) {
+MLA_EXPORT mla_status mla_decode_kvcache(const mla_decode_args* a, void* stream) {
   return decode_impl(a, stream, 3);
 }
 
-MLA_EXPORT int mla_decode_partial(const mla_decode_args* a, void* stream) {
+MLA_EXPORT mla_status mla_decode_partial(const mla_decode_args* a, void* stream) {
   return decode_impl(a, stream, 1);
 }
 
-MLA_EXPORT int mla_decode_combine(const mla_decode_args* a, void* stream) {
+MLA_EXPORT mla_status mla_decode_combine(const mla_decode_args* a, void* stream) {
   return decode_impl(a, stream, 2);
 }
 
 namespace {
 
 template <typename T>
-int copy_to_host(std::vector<T>* dst, const void* src, size_t n, hipStream_t s, const char* what) {
+mla_status copy_to_host(std::vector<T>* dst, const void* src, size_t n, hipStream_t s, const char* what) {
   dst->resize(n);
   if (n == 0) return MLA_OK;
   const hipError_t e = hipMemcpyAsync(dst->data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s);
@@ -294,45 +294,24 @@ int window_of(const mla_decode_args* a, int L, int s) {
 
 }  // namespace
 
-// Host-side audit of the device-resident values the kernels trust.  Every
-// buffer is copied to the host once; the checks below run there.
-MLA_EXPORT int mla_validate_inputs(const mla_decode_args* a, void* stream) {
-  int st = check_decode_args(a);
-  if (st != MLA_OK) return st;
-  if (a->batch == 0) return ok();
-  size_t ob;
-  st = check_workspace(a, &ob);
-  if (st != MLA_OK) return st;
+namespace {
+
+// The audit's checks on host copies of the buffers a decode call reads: L
+// [batch], bt [batch * max_blocks_per_seq], idx [units * topk] (NULL when
+// dense), md [the schedule's elements for the call's part and unit counts;
+// only the header is read if those do not match], ns [units + 1].
+mla_status audit_host(const mla_decode_args* a, const int32_t* L, const int32_t* bt, const int32_t* idx,
+                      const int32_t* md, const int32_t* ns) {
   if (a->num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
   const bool sparse = a->topk > 0;
   const int B = a->batch, U = units_of(a->batch, a->s_q, a->topk), P = a->num_parts;
   const size_t mb = (size_t)a->max_blocks_per_seq;
-  hipStream_t s = (hipStream_t)stream;
-  auto sync = [&]() {
-    const hipError_t e = hipStreamSynchronize(s);
-    return e == hipSuccess ? MLA_OK : fail(MLA_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
-  };
-  // The schedule's header first: a schedule built for another part or unit
-  // count has another size, so nothing past the header is read before the
-  // counts are known to match.
-  std::vector<int32_t> L, bt, idx, md, ns;
-  if ((st = copy_to_host(&md, a->tile_metadata, mla::kHeader, s, "tile_metadata")) != MLA_OK ||
-      (st = sync()) != MLA_OK)
-    return st;
-  if (md[5] != 0x4D4C4131)
+  if (md[5] != mla::kMagic)
     return fail(MLA_ERR_INVALID_ARGUMENT, "tile_metadata was not written by mla_get_metadata");
   if (md[0] != P || md[3] != U)
     return fail(MLA_ERR_INVALID_ARGUMENT,
                 "tile_metadata is for %d parts and %d units, the call has %d and %d", md[0], md[3],
                 P, U);
-  if ((st = copy_to_host(&L, a->cache_seqlens, B, s, "cache_seqlens")) != MLA_OK ||
-      (st = copy_to_host(&bt, a->block_table, B * mb, s, "block_table")) != MLA_OK ||
-      (st = copy_to_host(&idx, a->indices, sparse ? (size_t)U * a->topk : 0, s, "indices")) != MLA_OK ||
-      (st = copy_to_host(&md, a->tile_metadata, md_elems(U, P), s, "tile_metadata")) != MLA_OK ||
-      (st = copy_to_host(&ns, a->num_splits, (size_t)U + 1, s, "num_splits")) != MLA_OK ||
-      (st = sync()) != MLA_OK)
-    return st;
-
   // Sequence lengths, and the pool page of every block a visible key lies in.
   for (int b = 0; b < B; ++b) {
     if (L[b] < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seqlens[%d] = %d is negative", b, L[b]);
@@ -367,13 +346,13 @@ MLA_EXPORT int mla_validate_inputs(const mla_decode_args* a, void* stream) {
   // The schedule must be the one mla_get_metadata builds for these lengths
   // (and indices): header, blocks per unit, and parts that cover every
   // (unit, block) once, in order, with split indices counted by num_splits.
-  const int32_t* hdr = md.data();
-  const int32_t* nblk = md.data() + mla::kHeader + (size_t)mla::kPartRow * P;
+  const int32_t* hdr = md;
+  const int32_t* nblk = md + mla::kHeader + (size_t)mla::kPartRow * P;
   long long total = 0;
   for (int u = 0; u < U; ++u) {
     int want;
     if (!sparse) {
-      want = (L[u] + mla::kPage - 1) / mla::kPage;
+      want = (int)(((long long)L[u] + mla::kPage - 1) / mla::kPage);
     } else {
       // Blocks up to the last entry that indexes the sequence.
       const int Lb = L[u / a->s_q];
@@ -396,7 +375,7 @@ MLA_EXPORT int mla_validate_inputs(const mla_decode_args* a, void* stream) {
   int cu = 0, cj = 0;   // next (unit, block) to be covered
   int last_u = -1, next_split = 0;
   for (int p = 0; p < P; ++p) {
-    const int32_t* r = md.data() + mla::kHeader + (size_t)mla::kPartRow * p;
+    const int32_t* r = md + mla::kHeader + (size_t)mla::kPartRow * p;
     if (r[0] < 0) continue;
     const int u0 = r[0], j0 = r[1], u1 = r[2], j1 = r[3];
     if (u0 != cu || j0 != cj || u1 < u0 || u1 >= U || j1 < 1 || j1 > nblk[u1] ||
@@ -434,7 +413,57 @@ MLA_EXPORT int mla_validate_inputs(const mla_decode_args* a, void* stream) {
   return ok();
 }
 
-MLA_EXPORT int mla_append_kv(const void* rows, const int32_t* slots, int n, int kv_format, void* kcache,
+}  // namespace
+
+// Host-side audit of the device-resident values the kernels trust.  Every
+// buffer is copied to the host once; audit_host checks them there.
+MLA_EXPORT mla_status mla_validate_inputs(const mla_decode_args* a, void* stream) {
+  mla_status st = check_decode_args(a);
+  if (st != MLA_OK) return st;
+  if (a->batch == 0) return ok();
+  size_t ob;
+  st = check_workspace(a, &ob);
+  if (st != MLA_OK) return st;
+  if (a->num_pages < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  const bool sparse = a->topk > 0;
+  const int B = a->batch, U = units_of(a->batch, a->s_q, a->topk), P = a->num_parts;
+  const size_t mb = (size_t)a->max_blocks_per_seq;
+  hipStream_t s = (hipStream_t)stream;
+  auto sync = [&]() {
+    const hipError_t e = hipStreamSynchronize(s);
+    return e == hipSuccess ? MLA_OK : fail(MLA_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  };
+  // The schedule's header first: a schedule built for another part or unit
+  // count has another size, so nothing past the header is read before the
+  // counts are known to match.
+  std::vector<int32_t> L, bt, idx, md, ns;
+  if ((st = copy_to_host(&md, a->tile_metadata, mla::kHeader, s, "tile_metadata")) != MLA_OK ||
+      (st = sync()) != MLA_OK)
+    return st;
+  if (md[5] != mla::kMagic || md[0] != P || md[3] != U) return audit_host(a, nullptr, nullptr, nullptr, md.data(), nullptr);
+  if ((st = copy_to_host(&L, a->cache_seqlens, B, s, "cache_seqlens")) != MLA_OK ||
+      (st = copy_to_host(&bt, a->block_table, (size_t)B * mb, s, "block_table")) != MLA_OK ||
+      (st = copy_to_host(&idx, a->indices, sparse ? (size_t)U * a->topk : 0, s, "indices")) != MLA_OK ||
+      (st = copy_to_host(&md, a->tile_metadata, md_elems(U, P), s, "tile_metadata")) != MLA_OK ||
+      (st = copy_to_host(&ns, a->num_splits, (size_t)U + 1, s, "num_splits")) != MLA_OK ||
+      (st = sync()) != MLA_OK)
+    return st;
+  return audit_host(a, L.data(), bt.data(), sparse ? idx.data() : nullptr, md.data(), ns.data());
+}
+
+// The same audit on buffers the caller already holds in host memory.
+MLA_EXPORT mla_status mla_validate_host_inputs(const mla_decode_args* a, const int32_t* cache_seqlens,
+                                               const int32_t* block_table, const int32_t* indices,
+                                               const int32_t* tile_metadata, const int32_t* num_splits) {
+  mla_status st = check_decode_shape(a);
+  if (st != MLA_OK) return st;
+  if (a->batch == 0) return ok();
+  if (!cache_seqlens || !block_table || !tile_metadata || !num_splits || (a->topk > 0 && !indices))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a required host pointer is NULL");
+  return audit_host(a, cache_seqlens, block_table, a->topk > 0 ? indices : nullptr, tile_metadata, num_splits);
+}
+
+MLA_EXPORT mla_status mla_append_kv(const void* rows, const int32_t* slots, int n, int kv_format, void* kcache,
                              int num_pages, void* stream) {
   if (n < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n must be >= 0 (got %d)", n);
   if (kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8_656)

@@ -20,13 +20,18 @@ from .splitkv_schedule import schedule, check_schedule, unit_blocks_dense, unit_
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mla_oracle.c")
-_LIB = os.path.join(_HERE, "libmla_oracle.so")
+# MLA_ORACLE_LIB selects another build of the same source (the sanitizer
+# test loads an instrumented copy that way).
+_LIB = os.environ.get("MLA_ORACLE_LIB") or os.path.join(_HERE, "libmla_oracle.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (-O2, OpenMP, no FMA contraction so every
-    product and sum rounds as written)."""
+    product and sum rounds as written).  A build selected by MLA_ORACLE_LIB
+    is the caller's and is left alone."""
+    if os.environ.get("MLA_ORACLE_LIB"):
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
@@ -119,3 +124,24 @@ def decode(inp, sel=None, threads: int = 0):
     return decode_raw(inp.q, inp.kcache, inp.fmt, inp.block_table, inp.seqlens,
                       inp.indices, inp.softmax_scale, inp.causal, sel=sel,
                       threads=threads)
+
+
+def merge_partials(lse_parts, o_parts):
+    """Log-sum-exp merge of partial results over disjoint key sets (the
+    pieces num_splits counts; topnet.top "Was ist FlashMLA?",
+    "MLA-Metadaten abrufen"), in fp64.  lse_parts [k, n], o_parts
+    [k, n, d], each piece's output normalised by its own row sum:
+        lse = log sum_i exp(lse_i),  out = sum_i exp(lse_i - lse) * o_i,
+    and out = 0, lse = -inf where every piece is empty (lse_i = -inf)."""
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    with np.errstate(invalid="ignore"):
+        w = np.exp(lse_parts - m_safe[None, :])          # exp(-inf) = 0
+    total = w.sum(axis=0)
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, total)))
+    weights = np.where(empty[None, :], 0.0, np.exp(lse_parts - np.where(empty, 0.0, lse)[None, :]))
+    out = (weights[:, :, None] * o_parts).sum(axis=0)
+    return out, lse

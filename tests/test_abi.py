@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "mla.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(mla_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|mla_status|const char \*)\s*(mla_\w+)\s*\(", src, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -166,3 +166,26 @@ def test_append_rejects_bad_arguments_without_launching(lib):
     assert lib.mla_append_kv(None, fake, 4, 1, fake, 4, None) == -1
     assert lib.mla_append_kv(ctypes.c_void_p(0x1008), fake, 4, 1, fake, 4, None) == -1   # misaligned
     assert b"aligned" in lib.mla_last_error()
+
+
+def test_status_returning_calls_are_declared_so():
+    """Every entry point except the version and the error text returns an
+    mla_status."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    status = set(re.findall(r"^\s*mla_status\s+(mla_\w+)\s*\(", src, flags=re.M))
+    assert status == set(declared_functions()) - {"mla_version", "mla_last_error"}
+
+
+def test_python_decode_signature_follows_the_boundary():
+    """mla_decode_kvcache(q, kcache, block_table, cache_seqlens,
+    softmax_scale=None, causal=False, indices=None, metadata=None): the
+    schedule is optional (built on the call's stream when omitted)."""
+    import inspect
+    from mla_paged_kv_metadata_amd import mla_decode_kvcache
+    sig = inspect.signature(mla_decode_kvcache)
+    names = list(sig.parameters)
+    assert names[:8] == ["q", "kcache", "block_table", "cache_seqlens", "softmax_scale", "causal",
+                         "indices", "metadata"]
+    for n in ("softmax_scale", "indices", "metadata"):
+        assert sig.parameters[n].default is None
+    assert sig.parameters["causal"].default is False

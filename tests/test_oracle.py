@@ -258,3 +258,46 @@ def test_bad_block_table_is_reported(oracle_mod):
     inp.block_table[0, 1] = inp.num_pages + 5
     with pytest.raises(ValueError):
         oracle_mod.decode(inp)
+
+
+def test_merge_of_disjoint_key_sets_equals_the_whole(oracle_mod):
+    """Log-sum-exp merge identity, pinned on the decode oracle itself: split
+    every sequence's keys into three disjoint sets (sparse index lists),
+    decode each set alone and merge the pieces; the result equals the dense
+    decode over all keys.  Empty pieces (lse = -inf) drop out; a row whose
+    pieces are all empty merges to out = 0, lse = -inf."""
+    seqlens = [130, 1, 77, 0]
+    cfg = gen.small_config(len(seqlens), 1, 4, seqlens, seed=21)
+    inp = gen.make_inputs(cfg)
+    o_all, l_all = oracle_mod.decode(inp)
+    rng = np.random.default_rng(4)
+    topk = max(seqlens)
+    pieces_o, pieces_l = [], []
+    owner = [rng.integers(0, 3, size=L) for L in seqlens]   # piece of every key
+    for piece in range(3):
+        idx = np.full((len(seqlens), 1, topk), -1, dtype=np.int32)
+        for b, L in enumerate(seqlens):
+            keys = np.nonzero(owner[b] == piece)[0]
+            idx[b, 0, :keys.size] = keys
+        o, l = oracle_mod.decode(dataclasses.replace(inp, indices=idx))
+        pieces_o.append(o)
+        pieces_l.append(l)
+    out, lse = oracle_mod.merge_partials(np.stack(pieces_l), np.stack(pieces_o))
+    fin = np.isfinite(l_all)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(l_all))
+    np.testing.assert_allclose(lse[fin], l_all[fin], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out, o_all, rtol=1e-11, atol=1e-13)
+    assert np.all(out[~fin] == 0)
+
+
+def test_merge_closed_forms(oracle_mod):
+    """Two pieces of equal lse c: lse = c + ln 2, out = the mean of the two;
+    one piece: itself; a piece of lse -inf: no weight."""
+    o = np.array([[[1.0, -2.0]], [[3.0, 4.0]]])
+    out, lse = oracle_mod.merge_partials(np.array([[0.5], [0.5]]), o)
+    assert abs(lse[0] - (0.5 + math.log(2))) <= 1e-15
+    np.testing.assert_allclose(out[0], [2.0, 1.0], rtol=0, atol=1e-15)
+    out, lse = oracle_mod.merge_partials(np.array([[-1.25], [-np.inf]]), o)
+    assert lse[0] == -1.25 and np.array_equal(out[0], [1.0, -2.0])
+    out, lse = oracle_mod.merge_partials(np.array([[-np.inf], [-np.inf]]), o)
+    assert np.isneginf(lse[0]) and np.all(out[0] == 0)
