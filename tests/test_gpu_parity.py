@@ -313,7 +313,7 @@ def _visible_v(inp, b, keys):
     table (bf16 pool)."""
     keys = np.asarray(keys, dtype=np.int64)
     pages = inp.block_table[b, keys >> 6].astype(np.int64)
-    rows = inp.kcache.reshape(-1, 576)[pages * 64 + (keys & 63)]
+    rows = inp.kcache.view(np.uint16).reshape(-1, 576)[pages * 64 + (keys & 63)]
     return gen.bf16_bits_to_f32(rows[:, :512]).astype(np.float64)
 
 
@@ -485,3 +485,21 @@ def test_narrow_pieces_longer_than_64_pages(oracle_mod, fmt, parts, s_q):
     o, l, _ = run_gpu(inp, num_parts=parts)
     ro, rl = oracle_mod.decode(inp)
     compare(o, l, ro, rl, fmt, f"narrow long fmt={fmt} parts={parts} s_q={s_q}", inp=inp)
+
+
+def test_schedule_built_when_metadata_is_omitted():
+    """mla_decode_kvcache without `metadata` builds the step's schedule on
+    its own stream: same result, bit for bit, as with the schedule passed."""
+    from mla_paged_kv_metadata_amd import get_mla_metadata, mla_decode_kvcache
+    from gpu_util import to_device
+    cfg = gen.small_config(4, 2, 16, [700, 1, 2048, 129], causal=True, seed=50)
+    inp = gen.make_inputs(cfg, poison=True)
+    q, k, bt, sl, _ = to_device(inp)
+    md = get_mla_metadata(sl, 2 * 16, 1, s_q=2)
+    o1, l1 = mla_decode_kvcache(q, k, bt, sl, inp.softmax_scale, True, metadata=md)
+    o2, l2 = mla_decode_kvcache(q, k, bt, sl, inp.softmax_scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ro, rl = __import__("oracle").decode(inp)
+    compare(o2.float().cpu().numpy().reshape(-1, 512).astype(np.float64),
+            l2.cpu().numpy().reshape(-1).astype(np.float64), ro, rl, gen.FMT_BF16, "default metadata")
