@@ -180,6 +180,21 @@ mla_status mla_workspace_size(const mla_decode_args *args, size_t *bytes);
 mla_status mla_decode_kvcache(const mla_decode_args *args, void *stream);
 
 /*
+ * mla_decode_kvcache for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): args->workspace and args->workspace_bytes are ignored and the
+ * split partials go to the library's own device scratch, a static array of
+ * 96 MiB (100,663,296 bytes) that each device the library runs on holds
+ * until the process ends.  Calls whose workspace (mla_workspace_size) would
+ * exceed it return MLA_ERR_WORKSPACE_TOO_SMALL before launching anything.
+ * Allocates nothing.  All calls on one device share that device's scratch:
+ * calls that overlap in time on one device (other streams or threads) race
+ * and must not be issued.  Same arguments, results and other errors as
+ * mla_decode_kvcache.
+ */
+mla_status mla_decode_kvcache_noalloc(const mla_decode_args *args, void *stream);
+
+/*
  * The two halves of mla_decode_kvcache (same passages: the per-layer decode
  * of topnet.top "Was ist FlashMLA?", "MLA-Decodierung ausfuehren", and the
  * merge of the num_splits pieces of "MLA-Metadaten abrufen"), for callers

@@ -28,6 +28,7 @@ EXPORTED = (
     "mla_get_metadata",
     "mla_workspace_size",
     "mla_decode_kvcache",
+    "mla_decode_kvcache_noalloc",
     "mla_decode_partial",
     "mla_decode_combine",
     "mla_validate_inputs",
@@ -92,6 +93,7 @@ def load() -> ctypes.CDLL:
     lib.mla_get_metadata.argtypes = [P, P, i, i, i, i, i, i, P, P, P]
     lib.mla_workspace_size.argtypes = [ctypes.POINTER(MlaDecodeArgs), ctypes.POINTER(sz)]
     lib.mla_decode_kvcache.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
+    lib.mla_decode_kvcache_noalloc.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
     lib.mla_decode_partial.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
     lib.mla_decode_combine.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
     lib.mla_validate_inputs.argtypes = [ctypes.POINTER(MlaDecodeArgs), P]
@@ -101,7 +103,8 @@ def load() -> ctypes.CDLL:
     lib.mla_last_error.restype = ctypes.c_char_p
     lib.mla_version.argtypes = []
     for name in ("mla_metadata_size", "mla_metadata_size_for_parts", "mla_get_metadata",
-                 "mla_workspace_size", "mla_decode_kvcache", "mla_decode_partial",
+                 "mla_workspace_size", "mla_decode_kvcache", "mla_decode_kvcache_noalloc",
+                 "mla_decode_partial",
                  "mla_decode_combine", "mla_validate_inputs", "mla_validate_host_inputs",
                  "mla_append_kv", "mla_version"):
         getattr(lib, name).restype = i

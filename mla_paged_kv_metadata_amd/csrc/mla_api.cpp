@@ -266,6 +266,29 @@ MLA_EXPORT mla_status mla_decode_kvcache(const mla_decode_args* a, void* stream)
   return decode_impl(a, stream, 3);
 }
 
+// mla_decode_kvcache with the library's own device scratch in place of the
+// caller's workspace: no allocation anywhere on this path.
+MLA_EXPORT mla_status mla_decode_kvcache_noalloc(const mla_decode_args* a, void* stream) {
+  mla_status st = check_decode_args(a);
+  if (st != MLA_OK) return st;
+  if (a->batch == 0) return ok();
+  size_t ob, need;
+  workspace_layout(units_of(a->batch, a->s_q, a->topk), a->num_parts,
+                   rows_per_unit(a->s_q, a->h_q, a->topk), &ob, &need);
+  void* ws = nullptr;
+  size_t cap = 0;
+  const hipError_t e = mla::scratch_for_current_device(&ws, &cap);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "device scratch lookup: %s", hipGetErrorString(e));
+  if (need > cap)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of scratch; the library's device scratch holds %zu "
+                "(use mla_decode_kvcache with a workspace)", need, cap);
+  mla_decode_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = cap;
+  return decode_impl(&b, stream, 3);
+}
+
 MLA_EXPORT mla_status mla_decode_partial(const mla_decode_args* a, void* stream) {
   return decode_impl(a, stream, 1);
 }

@@ -13,10 +13,47 @@
 // the pieces of a unit.  The partial-attention kernels are chosen by the
 // number of query rows per unit: 16-row tiles (mla_decode_narrow.hip) for
 // up to 32 rows, 128-row tiles (mla_decode_wide.hip) above.
+#include <mutex>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
+
+// ---------------------------------------------------------------------------
+// Device scratch of mla_decode_kvcache_noalloc, for callers that cannot
+// allocate: the split partials of one decode call, kScratchBytes at most.
+// Every device the library runs on holds its own copy until the process
+// ends; each call on a device overwrites it (calls that overlap on one
+// device race).  Host code never uses the array's name as an address: its
+// device address is looked up once per device (scratch_for_current_device).
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)96 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t scratch_for_current_device(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = kScratchBytes;
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------------------
 // Combine: merge the k_u partial results of every split unit.

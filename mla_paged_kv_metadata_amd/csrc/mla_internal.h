@@ -42,6 +42,9 @@ hipError_t launch_wide(const DecodeParams& p, int kv_format, dim3 grid, hipStrea
 hipError_t launch_narrow(const DecodeParams& p, int kv_format, dim3 grid, hipStream_t stream);
 // which: 1 = split-KV attention kernel, 2 = combine kernel, 3 = both.
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int which, hipStream_t stream);
+// The device address and size of the library's scratch array on the
+// current device (mla_decode.hip; looked up once per device).
+hipError_t scratch_for_current_device(void** ptr, size_t* bytes);
 // Writing tokens into the pool (mla_append.hip): row i to pool row
 // slots[i] unless it lies outside [0, pool_rows).
 hipError_t launch_append(const void* rows, const int32_t* slots, int n, int kv_format, void* kcache,
