@@ -3,48 +3,51 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
-One step = one pass of the whole decode path over one batch: the split-KV
-schedule (mla_get_metadata), the split-KV attention kernel and the combine
-kernel, enqueued on one stream.  The workload is the memory-bound
-variable-length decode (batch 64, 1 query token, 16 heads, lengths uniform
-in [1, 8192], bf16 pages); `value` is its KV-read bandwidth (algorithmic KV
-bytes / step time).  The compute-bound MTP decode (batch 128, 2 query
-tokens, 128 heads, L = 4096, causal) is timed the same way and reported in
-bf16 TFLOPS under "mtp"; the FP8 and sparse workloads under "fp8"/"sparse".
+The decode of one layer is the split-KV attention kernel and the combine of
+split sequences, run with a schedule built once per decode step and shared
+by every layer (topnet.top "Was ist FlashMLA?", "MLA-Metadaten abrufen").
+A step here is that per-layer decode over one batch; `value` is its KV-read
+bandwidth on the memory-bound variable-length workload (batch 64, 1 query
+token, 16 heads, lengths uniform in [1, 8192], bf16 pages): algorithmic KV
+bytes / decode time.  The step including the schedule kernel is reported as
+`step_with_schedule_ms`.  The compute-bound MTP decode (batch 128, 2 query
+tokens, 128 heads, L = 4096, causal) is the metric's bf16-TFLOPS leg
+(`roofline_mtp`); the FP8, sparse, prefill and append workloads are under
+`secondary`.
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Six physical copies of each page pool (same logical cache, pages shuffled
-differently; --replicas) are used in rotation so that consecutive steps do
+differently; --replicas) are used in rotation so that consecutive calls do
 not hit the 256 MB Infinity Cache.
 
-Timed loops per workload:
-  * the steps replayed from HIP graphs, as a serving loop runs them: one
-    graph holds four rotations of consecutive steps (one step per pool copy,
-    each step complete: schedule, split-KV kernel, combine), so the launch
-    overhead of a graph is shared by 24 steps; wall time per step gives
-    `value` / `ms_per_step`.  Every graph's output is checked bit for bit
-    against an eager step first.
-  * the split-KV kernel alone, replayed from a graph of back-to-back
-    launches (one per pool copy) with HIP events on the launch stream
-    around the replays: its mean launch duration gives the roofline's
-    `achieved` (algorithmic bytes or flops per launch over it).
-  * the same step launched eagerly with HIP events around each kernel
-    (timing_ms: per-kernel event times, which include dispatch latency).
+Timed loops per workload, all replayed from HIP graphs (as a serving loop
+runs them) with HIP events on the launch stream around every replay; a
+graph holds four rotations of the pool copies (24 calls), so one graph
+launch's idle time is shared by 24 calls:
+  * decode: per call, the split-KV kernel and the combine (value,
+    ms_per_step; mean and p10/p50/p90 over replays);
+  * step_with_schedule: per call, the schedule kernel, then the decode;
+  * the dominant kernel alone, back to back: its mean launch duration gives
+    the roofline's `achieved` (algorithmic bytes or flops per launch over
+    it), the figure rocprofv3's kernel trace of the same command reports.
+Every graph's output is checked bit for bit against an eager call first.
 `roofline.traffic` (measured HBM bytes per launch) is read from the
 committed counter summary in profiles/ when it was taken on the kernel
-sources as they are now, else null.
+sources as they are now, else null.  `sclk_mhz` is the shader clock sampled
+while the MTP graphs run.
 
-    python bench.py --pmc-run [membound|mtp|fp8|sparse]
+    python bench.py --pmc-run [membound|mtp|fp8|sparse|...]
 
-runs the workload that the counter summaries are taken on: for the
-memory-bound one a plain fp32 copy of known size first (the counters'
-calibration), then a few eager steps.
+runs the workload that the counter summaries are taken on: a plain fp32
+copy of known size first (the counters' calibration), then a few eager
+calls of the workload.
 
 Prints ONE JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -79,13 +82,21 @@ def algorithmic_bytes(inp) -> dict:
     return {"kv": kv, "total": kv + other}
 
 
+def _pcts(per_call_ms) -> dict:
+    a = np.asarray(per_call_ms, dtype=np.float64)
+    return {"mean": float(a.mean()), "p10": float(np.percentile(a, 10)), "p50": float(np.median(a)),
+            "p90": float(np.percentile(a, 90))}
+
+
 class Workload:
-    """Device-resident inputs (with pool replicas) and prepared calls."""
+    """Device-resident inputs (with pool replicas), prepared calls and the
+    HIP graphs the timed loops replay."""
 
     def __init__(self, name: str, replicas: int):
         import torch
         import mla_inputs as gen
         import mla_paged_kv_metadata_amd as m
+        self.name = name
         self.cfg = gen.WORKLOADS[name]
         t0 = time.time()
         self.inp = gen.make_inputs(self.cfg)
@@ -118,12 +129,22 @@ class Workload:
         self.bytes = algorithmic_bytes(inp)
         self.flops = inp.flops()
 
-    def step(self, i, ev=None):
+    def refresh(self, r):
         import mla_paged_kv_metadata_amd as m
-        c = self.calls[i % len(self.calls)]
+        m.refresh_mla_metadata(self.mds[r], self.seqlens, self.indices)
+
+    def dominant(self, c):
+        """Launch the workload's dominant kernel alone: the split-KV kernel."""
+        c.partial()
+
+    def eager(self, i, ev=None):
+        """One eager step (schedule, split-KV kernel, combine), with HIP
+        events between the kernels when ev is given."""
+        r = i % len(self.calls)
+        c = self.calls[r]
         if ev is not None:
             ev[0].record()
-        m.refresh_mla_metadata(self.mds[i % len(self.calls)], self.seqlens, self.indices)
+        self.refresh(r)
         if ev is not None:
             ev[1].record()
         c.partial()
@@ -133,125 +154,134 @@ class Workload:
         if ev is not None:
             ev[3].record()
 
-    def capture(self):
-        """HIP graphs holding consecutive whole steps, one step per pool copy
-        in rotation: graphs[n] runs steps on copies 0 .. n - 1, so a full
-        rotation is one graph launch (as a serving loop launches one graph
-        per decode step of many kernels, not one per kernel)."""
+    def _graph(self, body):
         import torch
-        import mla_paged_kv_metadata_amd as m
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(GRAPH_ROTATIONS):
+                for r, c in enumerate(self.calls):
+                    body(r, c)
+        return g
+
+    def capture(self):
+        """Graphs of GRAPH_ROTATIONS rotations over the pool copies: decode
+        calls, schedule + decode calls, and the dominant kernel alone."""
+        import torch
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for i in range(2 * len(self.calls)):
-                self.step(i)
+                self.eager(i)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        self.graphs = {}
-        for n in range(1, len(self.calls) + 1):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for r, c in enumerate(self.calls[:n]):
-                    m.refresh_mla_metadata(self.mds[r], self.seqlens, self.indices)
-                    c.partial()
-                    c.combine()
-            self.graphs[n] = g
-        # Several rotations in one graph, so that the GPU idle time of a
-        # graph launch is shared by more steps (a serving loop's graph holds
-        # the decode step of every layer).
-        self.graph_rot = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph_rot):
-            for _ in range(GRAPH_ROTATIONS):
-                for r, c in enumerate(self.calls):
-                    m.refresh_mla_metadata(self.mds[r], self.seqlens, self.indices)
-                    c.partial()
-                    c.combine()
-        # The split-KV kernel alone, once per pool copy, back to back: its
-        # launch duration measured without the dispatch latency that HIP
-        # events around a single eager launch include.
-        self.graph_k2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph_k2):
-            for c in self.calls:
-                c.partial()
+        self.per_graph = GRAPH_ROTATIONS * len(self.calls)
+        self.g_decode = self._graph(lambda r, c: c.run())
+        self.g_step = self._graph(lambda r, c: (self.refresh(r), c.run()))
+        self.g_dominant = self._graph(lambda r, c: self.dominant(c))
         torch.cuda.synchronize()
 
-    def check_graph(self):
-        """Each graph's out/lse must equal the eager step's, bit for bit (all
-        pool copies hold the same logical cache, so every step of a graph
-        writes the same result)."""
+    def check_graphs(self):
+        """Each graph's out/lse must equal the eager call's, bit for bit (all
+        pool copies hold the same logical cache)."""
         import torch
         c0 = self.calls[0]
-        self.step(0)
+        self.eager(0)
         torch.cuda.synchronize()
         ref_o, ref_l = c0.out.clone(), c0.lse.clone()
-        checks = list(self.graphs.items()) + [(GRAPH_ROTATIONS * len(self.calls), self.graph_rot)]
-        for n, g in checks:
+        for name, g in (("decode", self.g_decode), ("step", self.g_step)):
             c0.out.fill_(0)
             c0.lse.fill_(0)
             g.replay()
             torch.cuda.synchronize()
             if not (torch.equal(c0.out, ref_o) and torch.equal(c0.lse, ref_l)):
-                raise RuntimeError(f"graph of {n} steps differs from the eager step")
+                raise RuntimeError(f"{name} graph differs from the eager call")
 
-    def _replay_steps(self, steps: int):
-        full = len(self.calls)
-        big = GRAPH_ROTATIONS * full
-        for _ in range(steps // big):
-            self.graph_rot.replay()
-        rest = steps % big
-        for _ in range(rest // full):
-            self.graphs[full].replay()
-        if rest % full:
-            self.graphs[rest % full].replay()
-
-    def time_graph(self, steps: int, warmup: int) -> float:
+    def time_graph(self, g, calls: int) -> dict:
+        """Replay g until about `calls` calls have run (at least 3 replays),
+        with HIP events on the launch stream around every replay; per-call
+        ms (mean, p10/p50/p90 over replays)."""
         import torch
-        self._replay_steps(warmup)
+        reps = max(3, -(-calls // self.per_graph))
+        g.replay()
+        g.replay()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        self._replay_steps(steps)
+        evs[0].record()
+        for i in range(reps):
+            g.replay()
+            evs[i + 1].record()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / steps
+        per_call = [evs[i].elapsed_time(evs[i + 1]) / self.per_graph for i in range(reps)]
+        out = _pcts(per_call)
+        out["calls"] = reps * self.per_graph
+        return out
 
-    def time_k2(self, reps: int) -> float:
-        """Mean split-KV launch duration (ms) from HIP events on the launch
-        stream around replays of the graph of back-to-back launches."""
-        import torch
-        for _ in range(2):
-            self.graph_k2.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            self.graph_k2.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * len(self.calls))
-
-    def time(self, steps: int, warmup: int) -> dict:
+    def time_eager(self, steps: int, warmup: int) -> dict:
+        """Eager steps with HIP events between the kernels (the per-kernel
+        times include dispatch latency)."""
         import torch
         for i in range(warmup):
-            self.step(i)
+            self.eager(i)
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for i in range(steps):
-            self.step(i, evs[i])
+            self.eager(i, evs[i])
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        md_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-        part_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-        comb_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-        step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
         return {
-            "wall_ms_per_step": (t1 - t0) * 1e3 / steps,
-            "event_ms_per_step": float(step_ms.mean()),
-            "metadata_ms": float(md_ms.mean()),
-            "splitkv_ms": float(part_ms.mean()),
-            "splitkv_ms_median": float(np.median(part_ms)),
-            "combine_ms": float(comb_ms.mean()),
+            "metadata_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+            "splitkv_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+            "combine_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])),
+            "step_ms": float(np.mean([e[0].elapsed_time(e[3]) for e in evs])),
         }
+
+
+def sample_sclk(run, seconds: float):
+    """Shader clock (MHz) sampled while `run()` keeps the GPU busy for about
+    `seconds`: median and max of the samples, or None if no reader works."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def reader():
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            while not stop.is_set():
+                info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+                samples.append(float(info.get("clk", info.get("cur_clk", 0))))
+                time.sleep(0.02)
+            amdsmi.amdsmi_shut_down()
+            return
+        except Exception as e:  # noqa: BLE001 - fall back to the command-line tool
+            log(f"[bench] amdsmi clock read failed ({e}); trying rocm-smi")
+        import re
+        import subprocess
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+                d = json.loads(r.stdout)
+                for card in d.values():
+                    for k, v in card.items():
+                        if "sclk" in k.lower():
+                            mm = re.search(r"(\d+)\s*Mhz", str(v), re.I)
+                            if mm:
+                                samples.append(float(mm.group(1)))
+            except Exception:  # noqa: BLE001
+                return
+
+    t = threading.Thread(target=reader, daemon=True)
+    t.start()
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        run()
+    stop.set()
+    t.join(timeout=15)
+    vals = [v for v in samples if v > 0]
+    if not vals:
+        return None
+    return {"median": float(np.median(vals)), "max": float(max(vals)), "samples": len(vals)}
 
 
 def bench_append(reps: int) -> dict:
@@ -296,43 +326,52 @@ def bench_append(reps: int) -> dict:
     return out
 
 
-def cpu_baseline(inp, target_s: float) -> dict:
+def cpu_baseline(inp, target_s: float, unit: str, threads=None) -> dict:
     """The fp64 oracle on a bounded sample of the same workload: whole
     sequences (all their query rows), taken in order until about target_s of
-    CPU work; reported as KV-read GB/s over the sampled sequences."""
+    CPU work per run; the median of three runs, reported in the metric's
+    unit over the sampled sequences (KV-read GB/s, or TFLOP/s)."""
     import oracle
     oracle.build(force=False)
-    threads = oracle.max_threads()
-    # calibrate on the first sequence
+    threads = threads or oracle.max_threads()
     rows_per_b = inp.s_q * inp.h_q
-    sel0 = np.arange(rows_per_b, dtype=np.int32)
-    t0 = time.perf_counter()
-    oracle.decode(inp, sel=sel0, threads=threads)
-    t_first = time.perf_counter() - t0
-    keys0 = max(int(inp.seqlens[0]), 1)
-    per_key = t_first / keys0
-    nb = 1
-    keys = keys0
-    while nb < inp.batch and (keys + int(inp.seqlens[nb])) * per_key < target_s:
-        keys += int(inp.seqlens[nb])
-        nb += 1
-    sel = np.arange(nb * rows_per_b, dtype=np.int32)
-    t0 = time.perf_counter()
-    oracle.decode(inp, sel=sel, threads=threads)
-    dt = time.perf_counter() - t0
-    # A sample shorter than the target (the whole workload fits in it) is
-    # decoded again until about target_s of CPU work has been timed.
-    passes = 1
-    if dt < 0.5 * target_s:
-        passes = max(1, int(target_s / max(dt, 1e-3)))
+    row_bytes = 1152 if inp.fmt == 0 else 656
+
+    def run(nb):
+        sel = np.arange(nb * rows_per_b, dtype=np.int32)
         t0 = time.perf_counter()
-        for _ in range(passes):
-            oracle.decode(inp, sel=sel, threads=threads)
-        dt = time.perf_counter() - t0
-    kv = int(sum(int(inp.seqlens[b]) for b in range(nb))) * (1152 if inp.fmt == 0 else 656)
-    return {"value": kv * passes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+        oracle.decode(inp, sel=sel, threads=threads)
+        return time.perf_counter() - t0
+
+    # calibrate on the first sequence, then take whole sequences in order
+    per_seq = run(1)
+    nb = max(1, min(inp.batch, int(target_s / max(per_seq, 1e-4))))
+    times = sorted(run(nb) for _ in range(3))
+    dt = times[1]
+    sub = dataclasses.replace(inp, seqlens=inp.seqlens[:nb], q=inp.q[:nb], block_table=inp.block_table[:nb],
+                              indices=None if inp.indices is None else inp.indices[:nb])
+    kv = sub.kv_bytes_read()
+    flops = sub.flops()
+    value = kv / dt / 1e9 if unit == "GB/s" else flops / dt / 1e12
+    return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
             "sample": f"first {nb} of {inp.batch} sequences, all {rows_per_b} query rows each "
-                      f"({kv / 1e6:.1f} MB of KV rows), {passes} pass(es) in {dt:.1f} s"}
+                      f"({kv / 1e6:.1f} MB of KV rows, {flops / 1e9:.2f} GFLOP); median of 3 runs "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s)",
+            "kv_gbs": kv / dt / 1e9, "tflops": flops / dt / 1e12}
+
+
+def cpu_tiny_one_thread() -> dict:
+    """The oracle on the tiny workload (batch 2, 16 heads, lengths 37 and
+    130) with one thread: median of 5 runs."""
+    import mla_inputs as gen
+    import oracle
+    inp = gen.make_inputs(gen.WORKLOADS["tiny"])
+    ts = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        oracle.decode(inp, threads=1)
+        ts.append(time.perf_counter() - t0)
+    return {"ms": float(np.median(ts)) * 1e3, "cores": 1, "kind": "oracle", "sample": "tiny workload, whole"}
 
 
 # The dominant kernel of each workload, as rocprofv3 names it, and the
@@ -353,15 +392,20 @@ KERNEL_SOURCES = {
     "sparse_prefill": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
     "dense_prefill": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "narrow_kernel_membound_b64_h16_traffic.md")
-# Kernel trace + MFMA counter summaries of the compute-bound workloads.
-MFMA_FILES = {
-    "mtp": os.path.join(ROOT, "profiles", "offset_kernel_mtp_b128_sq2_h128_kernel_stats.md"),
-    "fp8": os.path.join(ROOT, "profiles", "wide_kernel_fp8_b64_h128_L8192_kernel_stats.md"),
-    "sparse": os.path.join(ROOT, "profiles", "wide_kernel_sparse_b32_h128_top2048_kernel_stats.md"),
-    "sparse_prefill": os.path.join(ROOT, "profiles", "wide_kernel_sparse_prefill_sq2048_h128_top2048_kernel_stats.md"),
-    "dense_prefill": os.path.join(ROOT, "profiles", "offset_kernel_dense_prefill_sq2048_h128_L8192_kernel_stats.md"),
+# Counter summaries in profiles/: kernel trace + MFMA counters, and HBM
+# traffic (FETCH_SIZE / WRITE_SIZE), per workload.
+PROFILE_STEM = {
+    "membound": "narrow_kernel_membound_b64_h16",
+    "mtp": "offset_kernel_mtp_b128_sq2_h128",
+    "fp8": "wide_kernel_fp8_b64_h128_L8192",
+    "sparse": "wide_kernel_sparse_b32_h128_top2048",
+    "sparse_prefill": "wide_kernel_sparse_prefill_sq2048_h128_top2048",
+    "dense_prefill": "offset_kernel_dense_prefill_sq2048_h128_L8192",
 }
+
+
+def _profile(name: str, kind: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{PROFILE_STEM[name]}_{kind}.md")
 
 
 def sources_sha(name: str) -> str:
@@ -377,9 +421,7 @@ def measured_traffic(name: str):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary (a line `traffic-json: {...}`), or None if there is none or it
     was taken on other kernel sources."""
-    if name != "membound":
-        return None
-    return _summary_json(TRAFFIC_FILE, "traffic-json", name)
+    return _summary_json(_profile(name, "traffic"), "traffic-json", name)
 
 
 def _summary_json(path: str, tag: str, name: str):
@@ -396,44 +438,80 @@ def _summary_json(path: str, tag: str, name: str):
 
 
 def measured_mfma(name: str):
-    """MFMA counter figures (MfmaUtil, MFMA flops) of the dominant kernel from
-    the committed summary, or None."""
-    return _summary_json(MFMA_FILES[name], "mfma-json", name) if name in MFMA_FILES else None
+    """Kernel trace and MFMA counter figures of the dominant kernel from the
+    committed summary, or None."""
+    return _summary_json(_profile(name, "kernel_stats"), "mfma-json", name)
 
 
 def pmc_run(which: str):
-    """The run the counter summaries are taken on: for the memory-bound
-    workload, first a plain copy of known size (fp32, 256 Mi elements: 1 GiB
-    read, 1 GiB written: the counters' calibration), then six eager steps of
-    the workload."""
+    """The run the counter summaries are taken on: a plain copy of known
+    size (fp32, 256 Mi elements: 1 GiB read, 1 GiB written: the counters'
+    calibration), then six eager calls of the workload's decode."""
     import torch
-    if which == "membound":
-        n = 256 * 1024 * 1024
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)   # one elementwise kernel: reads n*4 B, writes n*4 B
-        torch.cuda.synchronize()
-        del src, dst
-        torch.cuda.empty_cache()
-        log(f"[bench] copy of {n * 4} B x3")
+    n = 256 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)   # one elementwise kernel: reads n*4 B, writes n*4 B
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"[bench] copy of {n * 4} B x3")
     w = Workload(which, 3)
     for i in range(6):
-        w.step(i)
+        w.refresh(i % 3)
+        w.calls[i % 3].run()
     torch.cuda.synchronize()
-    log(f"[bench] pmc run done: 6 steps of {w.cfg.name} ({w.flops} flops per split-KV launch)")
+    log(f"[bench] pmc run done: 6 calls of {w.cfg.name} ({w.flops} flops, {w.bytes['total']} B per call)")
 
 
 def run_workload(name: str, replicas: int, steps: int, warmup: int):
-    import torch
     w = Workload(name, replicas)
     w.capture()
-    w.check_graph()
-    t = w.time(steps, warmup)
-    t["graph_ms_per_step"] = w.time_graph(steps, warmup)
-    t["splitkv_ms_eager_events"] = t["splitkv_ms"]
-    t["splitkv_ms"] = w.time_k2(max(3, steps // len(w.calls)))
+    w.check_graphs()
+    t = {"decode": w.time_graph(w.g_decode, steps), "step_with_schedule": w.time_graph(w.g_step, steps),
+         "dominant_kernel": w.time_graph(w.g_dominant, steps), "eager": w.time_eager(max(5, steps // 4), warmup)}
     return w, t
+
+
+def roofline_object(w, t, bound: str) -> dict:
+    """Roofline of the dominant kernel: algorithmic bytes (hbm) or flops
+    (mfma) per launch over its mean launch duration in the timed graphs."""
+    ms = t["dominant_kernel"]["mean"]
+    traffic = measured_traffic(w.name)
+    if bound == "hbm":
+        achieved, peak, unit = w.bytes["total"] / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = w.flops / (ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    r = {"kernel": KERNEL_NAMES[w.name], "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+         "unit": unit, "frac": round(achieved / peak, 4),
+         "traffic": None if traffic is None else int(traffic["bytes_per_launch"]),
+         "algorithmic_bytes": w.bytes["total"], "algorithmic_flops": w.flops,
+         "kernel_ms": round(ms, 5)}
+    if traffic is not None:
+        r["traffic_detail"] = {k: traffic[k] for k in ("fetch_bytes", "write_bytes", "fetch_factor",
+                                                       "write_factor") if k in traffic}
+    mf = measured_mfma(w.name)
+    if mf is not None:
+        r["rocprof"] = mf
+    return r
+
+
+def summary(w, t) -> dict:
+    dec = t["decode"]["mean"] * 1e-3
+    return {
+        "workload": w.cfg.name,
+        "decode_ms": {k: round(v, 5) for k, v in t["decode"].items()},
+        "step_with_schedule_ms": {k: round(v, 5) for k, v in t["step_with_schedule"].items()},
+        "dominant_kernel": KERNEL_NAMES[w.name],
+        "dominant_kernel_ms": {k: round(v, 5) for k, v in t["dominant_kernel"].items()},
+        "eager_ms": {k: round(v, 5) for k, v in t["eager"].items()},
+        "tflops": round(w.flops / dec / 1e12, 2),
+        "kv_gbs": round(w.bytes["kv"] / dec / 1e9, 1),
+        "flops": w.flops,
+        "kv_bytes": w.bytes["kv"],
+        "num_parts": w.md.num_parts,
+    }
 
 
 def main():
@@ -442,13 +520,13 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--replicas", type=int, default=6)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=5.0, help="CPU work per oracle run (3 runs each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true",
-                    help="skip the MTP, FP8 and sparse workloads")
-    ap.add_argument("--only", choices=["mtp", "fp8", "sparse", "sparse_prefill", "dense_prefill", "append"],
-                    default=None,
-                    help="time just this secondary workload (for profiling)")
+                    help="skip every workload but the memory-bound one")
+    ap.add_argument("--only", choices=["membound", "mtp", "fp8", "sparse", "sparse_prefill", "dense_prefill",
+                                       "append"], default=None,
+                    help="time just this workload (for profiling)")
     ap.add_argument("--pmc-run", nargs="?", const="membound", default=None,
                     choices=["membound", "mtp", "fp8", "sparse", "sparse_prefill", "dense_prefill"],
                     help="the run hardware counters are collected on (no timing)")
@@ -473,17 +551,14 @@ def main():
         return
     if args.only is not None:
         w, t = run_workload(args.only, args.replicas, args.steps, args.warmup)
-        print(json.dumps({"workload": w.cfg.name, "timing_ms": t,
-                          "splitkv_tflops": w.flops / (t["splitkv_ms"] * 1e-3) / 1e12}), flush=True)
+        print(json.dumps(summary(w, t)), flush=True)
         return
 
     prim, tm = run_workload("membound", args.replicas, args.steps, args.warmup)
     log("[bench] membound timed")
     kv = prim.bytes["kv"]
-    step_ms = tm["graph_ms_per_step"]
-    value = kv / (step_ms * 1e-3) / 1e9
-    achieved = prim.bytes["total"] / (tm["splitkv_ms"] * 1e-3) / 1e9
-    traffic = measured_traffic("membound")
+    dec_ms = tm["decode"]["mean"]
+    value = kv / (dec_ms * 1e-3) / 1e9
     result = {
         "metric": "MLA paged decode: KV-read GB/s (h_q=16) and bf16 TFLOPS (h_q=128,s_q=2)",
         "value": round(value, 1),
@@ -491,7 +566,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
+        "ms_per_step": round(dec_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -504,52 +579,26 @@ def main():
             "sum_seqlens": int(prim.inp.seqlens.sum()),
             "kv_bytes": kv, "kv_format": "bf16", "page_size": 64,
             "num_parts": prim.md.num_parts, "pool_replicas": args.replicas,
-            "step": f"metadata + split-KV + combine, replayed from HIP graphs of "
-                    f"{GRAPH_ROTATIONS * args.replicas} consecutive steps",
+            "step": "one layer's decode (split-KV attention + combine) with the step's schedule, "
+                    f"replayed from HIP graphs of {GRAPH_ROTATIONS * args.replicas} calls",
         },
-        "timing_ms": {k: round(v, 5) for k, v in tm.items()},
-        # KV bytes over the decode kernels alone (split-KV + combine, HIP
-        # events), the schedule being built once per step for all layers.
-        "decode_kv_gbs": round(kv / ((tm["splitkv_ms"] + tm["combine_ms"]) * 1e-3) / 1e9, 1),
-        "roofline": {
-            "kernel": KERNEL_NAMES["membound"],
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if traffic is None else int(traffic["bytes_per_launch"]),
-            "algorithmic_bytes": prim.bytes["total"],
-        },
+        "timing_ms": summary(prim, tm),
+        "step_with_schedule_kv_gbs": round(kv / (tm["step_with_schedule"]["mean"] * 1e-3) / 1e9, 1),
+        "roofline": roofline_object(prim, tm, "hbm"),
     }
-    if traffic is not None:
-        result["roofline"]["traffic_detail"] = {k: traffic[k] for k in
-                                                ("fetch_bytes", "write_bytes", "fetch_factor", "write_factor")
-                                                if k in traffic}
     if not args.only_primary:
         extra = {}
         for key in ("mtp", "fp8", "sparse", "sparse_prefill", "dense_prefill"):
             del prim
             torch.cuda.empty_cache()
             log(f"[bench] timing {key}")
-            w, t = run_workload(key, args.replicas, max(10, args.steps // 2), args.warmup)
-            step_s = t["graph_ms_per_step"] * 1e-3
-            extra[key] = {
-                "workload": w.cfg.name,
-                "ms_per_step": round(t["graph_ms_per_step"], 5),
-                "tflops": round(w.flops / step_s / 1e12, 2),
-                "kv_gbs": round(w.bytes["kv"] / step_s / 1e9, 1),
-                "splitkv_kernel": KERNEL_NAMES[key],
-                "splitkv_ms": round(t["splitkv_ms"], 5),
-                "combine_ms": round(t["combine_ms"], 5),
-                "metadata_ms": round(t["metadata_ms"], 5),
-                "eager_ms_per_step": round(t["wall_ms_per_step"], 5),
-                "splitkv_tflops": round(w.flops / (t["splitkv_ms"] * 1e-3) / 1e12, 2),
-                "mfma_frac_of_bf16_peak": round(w.flops / (t["splitkv_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                "rocprof": measured_mfma(key),
-                "flops": w.flops,
-                "kv_bytes": w.bytes["kv"],
-            }
+            w, t = run_workload(key, args.replicas, max(24, args.steps // 2), args.warmup)
+            extra[key] = summary(w, t)
+            extra[key]["roofline"] = roofline_object(w, t, "mfma")
+            if key == "mtp":
+                result["roofline_mtp"] = extra[key]["roofline"]
+                result["sclk_mhz"] = sample_sclk(w.g_decode.replay, 1.5)
+                torch.cuda.synchronize()
             prim = w
         log("[bench] timing append")
         extra["append"] = bench_append(max(10, args.steps // 2))
@@ -557,9 +606,18 @@ def main():
         del prim
     if not args.no_cpu_baseline:
         import mla_inputs as gen
+        import oracle
         log("[bench] cpu baseline (oracle)")
+        oracle.build(force=False)
+        threads = oracle.max_threads()     # every host thread (read before any 1-thread run)
         inp = gen.make_inputs(gen.WORKLOADS["membound"])
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, "GB/s", threads)
+        if not args.only_primary:
+            for key in ("mtp", "fp8", "sparse"):
+                inp = gen.make_inputs(gen.WORKLOADS[key])
+                result["secondary"][key]["cpu_baseline"] = cpu_baseline(
+                    inp, args.cpu_seconds, "TFLOP/s" if key == "mtp" else "GB/s", threads)
+        result["cpu_baseline"]["tiny_one_thread"] = cpu_tiny_one_thread()
     print(json.dumps(result), flush=True)
 
 
