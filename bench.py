@@ -138,8 +138,8 @@ class Workload:
         c.partial()
 
     def eager(self, i, ev=None):
-        """One eager step (schedule, split-KV kernel, combine), with HIP
-        events between the kernels when ev is given."""
+        """One eager step (schedule, then the decode), with HIP events around
+        each when ev is given."""
         r = i % len(self.calls)
         c = self.calls[r]
         if ev is not None:
@@ -147,12 +147,9 @@ class Workload:
         self.refresh(r)
         if ev is not None:
             ev[1].record()
-        c.partial()
+        c.run()
         if ev is not None:
             ev[2].record()
-        c.combine()
-        if ev is not None:
-            ev[3].record()
 
     def _graph(self, body):
         import torch
@@ -223,16 +220,15 @@ class Workload:
         for i in range(warmup):
             self.eager(i)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
         for i in range(steps):
             self.eager(i, evs[i])
         torch.cuda.synchronize()
         return {
             "metadata_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
-            "splitkv_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
-            "combine_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])),
-            "step_ms": float(np.mean([e[0].elapsed_time(e[3]) for e in evs])),
+            "decode_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+            "step_ms": float(np.mean([e[0].elapsed_time(e[2]) for e in evs])),
         }
 
 
