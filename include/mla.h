@@ -90,6 +90,21 @@ typedef struct {
     float *lse;              /* [batch, s_q, h_q] fp32 natural-log
                                 log-sum-exp of the scaled scores (written);
                                 -inf and out = 0 where no key is visible */
+    int qk_fp8;              /* FP8 pools only.  0 (default): QK^T uses the
+                                query exactly (its e4m3 hi and remainder
+                                parts on the fp8 MFMA; products of codes
+                                and query values are exact).  1: the query
+                                is quantised to e4m3 per row and per half
+                                of its 512 NoPE dims, at a power-of-two
+                                scale 2^p with 2^(p+7) <= max |q| <
+                                2^(p+8), nearest value, ties to even (RoPE
+                                dims stay bf16), and QK^T runs on the fp8
+                                MFMA with half the operations (sao.pub
+                                FlashMLA overview, 一、项目速览: the FP8 cache
+                                and its sparse-decode throughput).  Needs an
+                                FP8 pool and more than 32 query rows per
+                                unit (s_q * h_q dense, h_q sparse), else
+                                MLA_ERR_UNSUPPORTED. */
 } mla_decode_args;
 
 /*

@@ -67,6 +67,7 @@ class MlaDecodeArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("out", ctypes.c_void_p),
         ("lse", ctypes.c_void_p),
+        ("qk_fp8", ctypes.c_int),
     ]
 
 

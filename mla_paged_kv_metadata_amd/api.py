@@ -96,7 +96,7 @@ def _kv_format(kcache: torch.Tensor) -> int:
 
 def make_args(q, kcache, block_table, cache_seqlens, metadata: MlaMetadata, out, lse,
               softmax_scale=None, causal=False, indices=None, workspace=None,
-              dv=D_V) -> _lib.MlaDecodeArgs:
+              dv=D_V, qk_fp8=False) -> _lib.MlaDecodeArgs:
     if q.dim() != 4 or q.dtype != torch.bfloat16 or not q.is_contiguous():
         raise ValueError("q must be a contiguous bf16 [batch, s_q, h_q, 576] tensor")
     if kcache.dim() != 4 or kcache.shape[1] != PAGE or not kcache.is_contiguous():
@@ -142,6 +142,7 @@ def make_args(q, kcache, block_table, cache_seqlens, metadata: MlaMetadata, out,
     a.num_splits = metadata.num_splits.data_ptr()
     a.out = out.data_ptr()
     a.lse = lse.data_ptr()
+    a.qk_fp8 = 1 if qk_fp8 else 0
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -159,12 +160,14 @@ def mla_decode_kvcache(q: torch.Tensor, kcache: torch.Tensor, block_table: torch
                        causal: bool = False, indices: Optional[torch.Tensor] = None,
                        metadata: Optional[MlaMetadata] = None, dv: int = D_V,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None):
+                       workspace: Optional[torch.Tensor] = None, qk_fp8: bool = False):
     """Decode one layer; returns (out [b, s_q, h_q, 512] bf16, lse [b, s_q, h_q] fp32).
 
     `metadata` is the step's schedule from get_mla_metadata, built once per
     decode step and passed to every layer; when it is omitted the schedule
-    is built here on the same stream (one more kernel launch)."""
+    is built here on the same stream (one more kernel launch).  qk_fp8
+    (FP8 pools, more than 32 query rows per unit): QK^T with the query
+    quantised to e4m3 per row half (see mla_decode_args.qk_fp8)."""
     lib = _lib.load()
     batch, s_q, h_q, _ = q.shape
     dev = q.device
@@ -176,7 +179,7 @@ def mla_decode_kvcache(q: torch.Tensor, kcache: torch.Tensor, block_table: torch
     if lse is None:
         lse = torch.empty(batch, s_q, h_q, dtype=torch.float32, device=dev)
     args = make_args(q, kcache, block_table, cache_seqlens, metadata, out, lse,
-                     softmax_scale=softmax_scale, causal=causal, indices=indices, dv=dv)
+                     softmax_scale=softmax_scale, causal=causal, indices=indices, dv=dv, qk_fp8=qk_fp8)
     with torch.cuda.device(dev):
         need = workspace_bytes(args)
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -223,13 +226,13 @@ class DecodeCall:
 
     def __init__(self, q, kcache, block_table, cache_seqlens, metadata: MlaMetadata,
                  softmax_scale=None, causal=False, indices=None, out=None, lse=None,
-                 workspace=None):
+                 workspace=None, qk_fp8=False):
         batch, s_q, h_q, _ = q.shape
         dev = q.device
         self.out = out if out is not None else torch.empty(batch, s_q, h_q, D_V, dtype=torch.bfloat16, device=dev)
         self.lse = lse if lse is not None else torch.empty(batch, s_q, h_q, dtype=torch.float32, device=dev)
         self.args = make_args(q, kcache, block_table, cache_seqlens, metadata, self.out, self.lse,
-                              softmax_scale=softmax_scale, causal=causal, indices=indices)
+                              softmax_scale=softmax_scale, causal=causal, indices=indices, qk_fp8=qk_fp8)
         need = workspace_bytes(self.args)
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

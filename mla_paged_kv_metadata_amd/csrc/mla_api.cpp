@@ -112,6 +112,11 @@ mla_status check_decode_shape(const mla_decode_args* a) {
     return fail(MLA_ERR_INVALID_ARGUMENT, "num_parts must be in [1, %d]", mla::kMaxParts);
   if (!std::isfinite(a->softmax_scale))
     return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (a->qk_fp8 != 0 && a->qk_fp8 != 1) return fail(MLA_ERR_INVALID_ARGUMENT, "qk_fp8 must be 0 or 1");
+  if (a->qk_fp8 && (a->kv_format != MLA_KV_FP8_656 || rows_per_unit(a->s_q, a->h_q, a->topk) <= 32))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "qk_fp8 needs an FP8 pool and more than 32 query rows per unit (the 16-row kernel "
+                "of the memory-bound shapes has no fp8 query path)");
   // Row counts are 32-bit in the kernels (every memory offset is 64-bit).
   if ((long long)std::max(a->batch, 1) * a->s_q * a->h_q > 0x7FFFFFFFLL)
     return fail(MLA_ERR_INVALID_ARGUMENT, "too many query rows (batch * s_q * h_q must be below 2^31)");
@@ -142,7 +147,7 @@ mla_status check_decode_args(const mla_decode_args* a) {
 
 }  // namespace
 
-MLA_EXPORT int mla_version(void) { return 1; }
+MLA_EXPORT int mla_version(void) { return 2; }
 
 MLA_EXPORT const char* mla_last_error(void) { return g_last_error.c_str(); }
 
@@ -255,6 +260,7 @@ mla_status decode_impl(const mla_decode_args* a, void* stream, int which) {
   p.causal = a->causal ? 1 : 0;
   p.num_pages = a->num_pages;
   p.scale_log2 = a->softmax_scale * mla::kLog2e;
+  p.qk8 = a->qk_fp8;
   hipError_t e = mla::launch_decode(p, a->kv_format, which, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();

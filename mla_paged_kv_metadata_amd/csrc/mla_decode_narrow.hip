@@ -229,8 +229,8 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
       const uint8_t* kb = rcur;
       if constexpr (FMT == 1) {
         if (vmask != 0u) {
-          dequant_slice<kThreads>(rcur, kbf);
-          dequant_slice<kThreads>(rcur + kSlice * kFp8RowBytes, kbf + kSliceBytes);
+          dequant_codes<kThreads>(rcur, kbf);
+          dequant_codes<kThreads>(rcur + kSlice * kFp8RowBytes, kbf + kSliceBytes);
         }
         lds_barrier();   // kbf holds page j
         kb = kbf;
@@ -243,15 +243,48 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
         const int ln = opaque_lane();
         const int t = 16 * (wave & 1) + (ln & 15);
         const int gg = ln >> 4;
-        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
+        f32x4 sres;
+        if constexpr (FMT == 1) {
+          // Exact codes: k-steps 4 G .. 4 G + 3 are NoPE group G, 16 and 17
+          // RoPE.  Each group's partial sums are multiplied by that group's
+          // scale of their key (the lane's output keys 16 (wave & 1) + 4 g
+          // + i of half wave >> 1: raw rows 32 (wave >> 1) + ...).
+          f32x4 sc4[4];
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ks += 2) {
-          const bf16x8 a0 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + gg));
-          const bf16x8 a1 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + 4 + gg));
-          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], sa, 0, 0, 0);
-          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], sb, 0, 0, 0);
+          for (int i = 0; i < 4; ++i) sc4[i] = fp8_scales(rcur, 32 * (wave >> 1) + 16 * (wave & 1) + 4 * gg + i);
+          f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f};
+          sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kh + slice_off(t, 64 + gg)), qf[16], sr,
+                                                       0, 0, 0);
+          sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kh + slice_off(t, 68 + gg)), qf[17], sr,
+                                                       0, 0, 0);
+#pragma unroll
+          for (int G = 0; G < 4; ++G) {
+            f32x4 ta = f32x4{0.f, 0.f, 0.f, 0.f}, tb = ta;
+#pragma unroll
+            for (int kk = 0; kk < 4; kk += 2) {
+              const int ks = 4 * G + kk;
+              const bf16x8 a0 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + gg));
+              const bf16x8 a1 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + 4 + gg));
+              ta = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], ta, 0, 0, 0);
+              tb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], tb, 0, 0, 0);
+            }
+            const f32x4 tg = ta + tb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sr[i] = __builtin_fmaf(tg[i], sc4[i][G], sr[i]);
+          }
+          sres = sr;
+        } else {
+          f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
+#pragma unroll
+          for (int ks = 0; ks < kKSteps; ks += 2) {
+            const bf16x8 a0 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + gg));
+            const bf16x8 a1 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + 4 + gg));
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], sb, 0, 0, 0);
+          }
+          sres = sa + sb;
         }
-        *(f32x4*)(xs + wave * 1024 + lane * 16) = sa + sb;
+        *(f32x4*)(xs + wave * 1024 + lane * 16) = sres;
       }
       lds_barrier();   // all four S^T tiles visible
       // ---- lane holds row l % 16 and keys 16 w + 4 g + i (i < 4) for w < 4.
@@ -309,9 +342,20 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
       // chunk 16 wave + 2 dt + ((j >> 1) & 1) of the half.
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        // FP8: wave w's V dims are NoPE group w; the probabilities times
+        // that group's scale of their key (page key 32 h + 16 (i >> 2) +
+        // 4 g + (i & 3) for e[8 h + i]).
+        float ev[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ev[i] = e[8 * h + i];
+          if constexpr (FMT == 1)
+            ev[i] *= *(const float*)(rcur + (32 * h + 16 * (i >> 2) + 4 * g + (i & 3)) * kFp8RowBytes +
+                                     kFp8ScaleOff + 4 * wave);
+        }
         const bf16x8 pb = __builtin_bit_cast(
-            bf16x8, u32x4{pack_bf16x2(e[8 * h + 0], e[8 * h + 1]), pack_bf16x2(e[8 * h + 2], e[8 * h + 3]),
-                          pack_bf16x2(e[8 * h + 4], e[8 * h + 5]), pack_bf16x2(e[8 * h + 6], e[8 * h + 7])});
+            bf16x8, u32x4{pack_bf16x2(ev[0], ev[1]), pack_bf16x2(ev[2], ev[3]), pack_bf16x2(ev[4], ev[5]),
+                          pack_bf16x2(ev[6], ev[7])});
         const uint8_t* vh = kb + h * kSliceBytes;
         const int ln = opaque_lane();
         const int jj = ln & 15;

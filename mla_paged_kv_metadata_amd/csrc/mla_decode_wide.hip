@@ -73,6 +73,7 @@ constexpr int kXchgBytes = 16 * 64 * 4;                   // one wave's S^T tile
 constexpr float kRescaleSlack = 8.f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Per-format geometry: ring slot size, copy instructions (64 lanes x 16 B)
 // per slice and per wave, and QL = k-steps of Q kept in LDS instead of
@@ -217,6 +218,193 @@ __device__ __forceinline__ f32x16 qk_partial(const uint8_t* kb, const bf16x8 (&q
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  return s;
+}
+
+// ---- FP8 pools: QK on the fp8 MFMA ----------------------------------------
+// The 512 NoPE dims of the scores come from v_mfma_scale_f32_32x32x64_f8f6f4
+// with the e4m3 codes of the raw slice as the A operand (exact, no
+// conversion) and the query as the B operand in e4m3, per row and per wave
+// half (dims 256 hf .. 256 hf + 255) scaled by a power of two 2^p: each
+// bf16 query value x / 2^p is split into hi = e4m3(x / 2^p) and
+// lo = e4m3(16 (x / 2^p - hi)), which is exact whenever the remainder's
+// exponent stays within e4m3's range (a bf16 value has 8 significant bits,
+// hi carries 4 and the remainder at most 4 more), and lo enters the MFMA
+// with the operand scale 2^-4.  With `lo` dropped (QLO = false) the query is
+// quantised to e4m3 per row half: half the MFMAs, with a relative error of
+// up to 2^-4 per query value, and the row half's scale is 2^p * alpha
+// with alpha = (x . x) / (x . hi) over its 256 dims (x = q / 2^p), which
+// makes the rounding error orthogonal to the query (attention weights keys
+// along q most, so this keeps the rounding from shifting all their scores
+// together).  The RoPE dims stay bf16.  The four group
+// scales of a key are applied to the partial sums (below), so no product
+// code * scale is ever rounded.
+
+// Per-slice scale table, written by the last wave (with 8 waves it has no
+// RoPE copy in dequant_slice): for wave half h and key t, groups 2 h and
+// 2 h + 1: scl[32 (2 h) + t] and scl[32 (2 h + 1) + t] the scales, and
+// scl[32 (4 + h) + t] their ratio (v_rcp_f32).  A group whose scale is 0
+// gets its 128 codes zeroed in the raw slice and scale 1, which gives the
+// same zeros (code * 0) and keeps the ratio finite.
+__device__ __forceinline__ void fp8_scale_table(uint8_t* raw, float* scl) {
+  const int w = (int)threadIdx.x - (kThreads - 64);
+  if (w < 0) return;
+  const int t = w & (kSlice - 1);
+  const int h = w >> 5;
+  uint8_t* row = raw + t * kFp8RowBytes;
+  const f32x2 sv = *(const f32x2*)(row + kFp8ScaleOff + 8 * h);
+  float s0 = sv[0], s1 = sv[1];
+  if (s0 == 0.f || s1 == 0.f) {
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i)
+      if ((i < 8 ? s0 : s1) == 0.f) *(u32x4*)(row + 256 * h + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    s0 = s0 == 0.f ? 1.f : s0;
+    s1 = s1 == 0.f ? 1.f : s1;
+  }
+  scl[kSlice * (2 * h) + t] = s0;
+  scl[kSlice * (2 * h + 1) + t] = s1;
+  scl[kSlice * (4 + h) + t] = s0 * __builtin_amdgcn_rcpf(s1);
+}
+
+// The query of one unit for the fp8 path: lane l holds row row_base + l % 32
+// and, for MFMA m = 0..3, NoPE dims 256 hf + 64 m + 32 (l / 32) .. + 31 in
+// qh[m] (and ql[m]) as 32 e4m3 bytes; the RoPE k-steps j = 0, 1 (dims
+// 512 + 32 hf + 16 j + 8 (l / 32) .. + 7) in qr[j] as bf16; *qsc = 2^p.
+// Rows past R are zero (p = 0).  A negative softmax scale negates q.
+template <bool QLO>
+__device__ __forceinline__ void load_q_fp8(const DecodeParams& p, int u, int row_base, int hf, bool qneg,
+                                           i32x8 (&qh)[4], i32x8 (&ql)[QLO ? 4 : 1], bf16x8 (&qr)[2],
+                                           float* qsc) {
+  const int lane = opaque_lane();
+  const int my_row = row_base + (lane & 31);
+  const bool row_ok = my_row < p.R;
+  const int hh = lane >> 5;
+  const uint8_t* qrow = p.q + ((size_t)u * p.R + (row_ok ? my_row : 0)) * (2 * kDqk);
+  const uint32_t neg = qneg ? 0x80008000u : 0u;
+  u32x4 v[4][4];   // [m][16-byte part]: 8 bf16 each
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      u32x4 x = *(const u32x4*)(qrow + 2 * (256 * hf + 64 * m + 32 * hh) + 16 * k);
+      v[m][k] = row_ok ? (x ^ neg) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    u32x4 x = *(const u32x4*)(qrow + 2 * (512 + 32 * hf + 16 * j + 8 * hh));
+    qr[j] = __builtin_bit_cast(bf16x8, row_ok ? (x ^ neg) : u32x4{0u, 0u, 0u, 0u});
+  }
+  // Largest magnitude over the row's 256 dims of this half (both lanes of
+  // the row), as bf16 bit patterns without sign.
+  uint32_t amax = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = v[m][k][e];
+        amax = max(amax, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
+      }
+  amax = max(amax, (uint32_t)__builtin_bit_cast(int, xor32(__builtin_bit_cast(float, (int)amax))));
+  // 2^p with p = (exponent of amax) - 7, so every |x| / 2^p < 256 <= 448;
+  // p = 0 for a zero row.  Scaling by powers of two is exact.
+  const int e = (int)(amax >> 7);                       // biased bf16/fp32 exponent
+  const int pe = amax == 0 ? 127 : max(e - 7, 1);       // biased exponent of 2^p
+  const float two_p = __builtin_bit_cast(float, pe << 23);
+  const float inv = __builtin_bit_cast(float, (254 - pe) << 23);   // 2^-p
+  float xx = 0.f, xh = 0.f;   // x . x and x . hi (QLO = false)
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    int hi[8], lo[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {   // 4 values -> one dword of e4m3
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = v[m][k][2 * e2 + (i >> 1)];
+          x[i] = __builtin_bit_cast(float, (i & 1) ? (w & 0xFFFF0000u) : (w << 16)) * inv;
+        }
+        int h = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+        h = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h, true);
+        hi[2 * k + e2] = h;
+        const f32x2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+        const f32x2 b1 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+        if constexpr (QLO) {
+          int l = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (x[0] - b0[0]), 16.f * (x[1] - b0[1]), 0, false);
+          l = __builtin_amdgcn_cvt_pk_fp8_f32(16.f * (x[2] - b1[0]), 16.f * (x[3] - b1[1]), l, true);
+          lo[2 * k + e2] = l;
+        } else {
+          xx += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+          xh += x[0] * b0[0] + x[1] * b0[1] + x[2] * b1[0] + x[3] * b1[1];
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qh[m][i] = hi[i];
+    if constexpr (QLO) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ql[QLO ? m : 0][i] = lo[i];
+    }
+  }
+  if constexpr (QLO) {
+    *qsc = two_p;
+  } else {
+    xx += xor32(xx);
+    xh += xor32(xh);
+    *qsc = two_p * (xh > 0.f ? xx / xh : 1.f);
+  }
+}
+
+// Partial S^T of this wave's half for FP8 pools: NoPE groups A = 2 hf (fp8
+// MFMAs m = 0, 1) and B = 2 hf + 1 (m = 2, 3) in one accumulator,
+// s = ((sum_A * scA / scB) + sum_B) * scB * 2^p, then the two RoPE k-steps
+// (bf16, from the decoded slice kb).  Output register r holds key
+// 8 (r >> 2) + 4 (l / 32) + (r & 3) of the slice for query row l % 32.
+template <bool QLO>
+__device__ __forceinline__ f32x16 qk_fp8(const uint8_t* raw, const uint8_t* kb, const float* scl,
+                                         const i32x8 (&qh)[4], const i32x8 (&ql)[QLO ? 4 : 1],
+                                         const bf16x8 (&qr)[2], float qsc, int hf) {
+  const int ln = opaque_lane();
+  const int t = ln & 31;
+  const int hh = ln >> 5;
+  const uint8_t* krow = raw + t * kFp8RowBytes + 256 * hf + 32 * hh;
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m == 2) {   // group A done: s *= scA / scB
+      const float* rA = scl + kSlice * (4 + hf) + 4 * hh;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 r4 = *(const f32x4*)(rA + 8 * j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[4 * j + i] *= r4[i];
+      }
+    }
+    const u32x4 a0 = *(const u32x4*)(krow + 64 * m);
+    const u32x4 a1 = *(const u32x4*)(krow + 64 * m + 16);
+    const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+    s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qh[m], s, 0, 0, 0, 127, 0, 127);
+    if constexpr (QLO) s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, ql[QLO ? m : 0], s, 0, 0, 0, 127, 0, 123);
+  }
+  {
+    const float* sB = scl + kSlice * (2 * hf + 1) + 4 * hh;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 b4 = *(const f32x4*)(sB + 8 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[4 * j + i] *= b4[i] * qsc;
+    }
+  }
+  const int sw = swz(t);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bf16x8 a = *(const bf16x8*)(kb + 8 * kGroupBytes + t * 128 + 16 * (((4 * hf + 2 * j + hh) ^ sw) & 7));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[j], s, 0, 0, 0);
+  }
   return s;
 }
 
@@ -433,11 +621,13 @@ __device__ __forceinline__ bool decode_item(const DecodeParams& p, Item& it) {
 }
 
 // ---- all eight waves in step (FP8 pages) ----------------------------------
-template <int FMT, bool SPARSE>
+// QLO (FP8): the query's e4m3 remainder part is used (exact products);
+// without it, the query is quantised to e4m3 per row half.
+template <int FMT, bool SPARSE, bool QLO = true>
 __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p) {
   using G = Geo<FMT>;
-  constexpr int QL = G::QL;
-  constexpr int QR = kKSteps - QL;
+  constexpr int QL = FMT == 1 ? 1 : G::QL;   // FP8: the whole query in registers
+  constexpr int QR = FMT == 1 ? 1 : kKSteps - QL;
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[G::kRingBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[G::kRingBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[G::kRingBytes];
@@ -445,6 +635,7 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
   __shared__ __attribute__((aligned(1024))) uint8_t xs[kWaves * kXchgBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t qs[kWaves * QL * 1024];
   __shared__ int32_t tab[SPARSE ? kTab : 1];
+  __shared__ __attribute__((aligned(16))) float scl[FMT == 1 ? 6 * kSlice : 4];   // FP8 scales, ratios
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -481,7 +672,13 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
     int tab_base = kPage * jb;
     if (SPARSE) fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
     bf16x8 qf[QR];
-    load_q(p, u, row_base, hf, qneg, qf, qs_mine);
+    i32x8 qh[FMT == 1 ? 4 : 1], ql[FMT == 1 && QLO ? 4 : 1];
+    bf16x8 qr[2];
+    float qsc = 1.f;
+    if constexpr (FMT == 1)
+      load_q_fp8<QLO>(p, u, row_base, hf, qneg, qh, ql, qr, &qsc);
+    else
+      load_q(p, u, row_base, hf, qneg, qf, qs_mine);
     wait_vmem<0>();
     lds_barrier();   // tab complete
 
@@ -528,12 +725,16 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
       ++sl;
       if (vmask == 0u) return;   // no visible key in this slice (uniform)
       const uint8_t* kb = rcur;
+      f32x16 s;
       if constexpr (FMT == 1) {
-        dequant_slice<kThreads>(rcur, kbf);
+        dequant_slice<kThreads>(rcur, kbf);   // V and RoPE, scaled bf16
+        fp8_scale_table(rcur, scl);
         lds_barrier();
         kb = kbf;
+        s = qk_fp8<QLO>(rcur, kb, scl, qh, ql, qr, qsc, hf);
+      } else {
+        s = qk_partial<QR>(kb, qf, qs_mine, hf);
       }
-      f32x16 s = qk_partial<QR>(kb, qf, qs_mine, hf);
       xchg_put(xs_mine, s, lane);
       lds_barrier();
       xchg_add(xs_peer, s, lane);
@@ -675,11 +876,16 @@ hipError_t launch_wide(const DecodeParams& p, int kv_format, dim3 grid, hipStrea
       hipLaunchKernelGGL((wide::wide_kernel<0, true>), grid, dim3(wide::kThreads), 0, stream, p);
     else
       hipLaunchKernelGGL((wide::offset_kernel), grid, dim3(wide::kThreads), 0, stream, p);
+  } else if (p.qk8) {
+    if (sparse)
+      hipLaunchKernelGGL((wide::wide_kernel<1, true, false>), grid, dim3(wide::kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((wide::wide_kernel<1, false, false>), grid, dim3(wide::kThreads), 0, stream, p);
   } else {
     if (sparse)
-      hipLaunchKernelGGL((wide::wide_kernel<1, true>), grid, dim3(wide::kThreads), 0, stream, p);
+      hipLaunchKernelGGL((wide::wide_kernel<1, true, true>), grid, dim3(wide::kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((wide::wide_kernel<1, false>), grid, dim3(wide::kThreads), 0, stream, p);
+      hipLaunchKernelGGL((wide::wide_kernel<1, false, true>), grid, dim3(wide::kThreads), 0, stream, p);
   }
   return hipGetLastError();
 }

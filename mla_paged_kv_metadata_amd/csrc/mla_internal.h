@@ -27,6 +27,7 @@ struct DecodeParams {
   int num_pages;               // pages in the pool (0: no key can be read)
   int causal;
   float scale_log2;            // softmax_scale * log2(e)
+  int qk8;                     // FP8 pools: query quantised to e4m3 (one fp8 MFMA per 64 dims)
 };
 
 // Rows one decode workgroup covers for a given number of rows per unit.

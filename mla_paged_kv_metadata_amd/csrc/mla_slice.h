@@ -161,6 +161,47 @@ __device__ __forceinline__ const uint8_t* bf16_copy_src(const DecodeParams& p, i
   return p.kcache + (size_t)row * kBf16RowBytes + 16 * ((ln & 7) ^ swz(t));
 }
 
+// Decode a raw FP8 slice for the MFMAs with the scales left out (all
+// THREADS threads): the 512 e4m3 NoPE codes of each key become bf16 values
+// equal to the codes themselves (every e4m3 value is exact in bf16;
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1.0), the 64 bf16 RoPE values are
+// copied, all into a bf16 slice `dst`.  The group scales stay in the raw
+// rows (fp8_scales) and are applied after the MFMAs: to the score partial
+// sums of each 128-dim group, and to the probabilities of each V group, so
+// that no product code * scale is ever rounded.
+template <int THREADS>
+__device__ __forceinline__ void dequant_codes(const uint8_t* raw, uint8_t* dst) {
+  static_assert((kSlice * 32) % THREADS == 0 && THREADS % 64 == 0, "whole items per thread");
+  // NoPE: item w is 16-code chunk k = w / 32 of key t = w % 32, so that a
+  // wave's lanes read 32 rows at one offset (the 656-byte row stride puts
+  // 16 lanes on 64 distinct banks) and write one chunk of 32 keys (the
+  // pattern the swizzle keeps conflict-free).  Every thread takes the same
+  // number of items and no lane branches.  One item at a time: the callers
+  // hold all their accumulators across this.
+#pragma unroll 1
+  for (int i = 0; i < kSlice * 32 / THREADS; ++i) {
+    const int w = threadIdx.x + THREADS * i;
+    const int t = w & (kSlice - 1);
+    const int k = w >> 5;
+    const u32x4 codes = *(const u32x4*)(raw + t * kFp8RowBytes + 16 * k);
+    uint32_t wv[8];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      wv[2 * qq] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)codes[qq], 1.0f, false));
+      wv[2 * qq + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)codes[qq], 1.0f, true));
+    }
+    *(u32x4*)(dst + slice_off(t, 2 * k)) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    *(u32x4*)(dst + slice_off(t, 2 * k + 1)) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+  }
+  // RoPE: 8 chunks of 8 bf16 per key, copied; item w is chunk w / 32 of key
+  // w % 32 (whole waves take part or skip).
+  for (int w = threadIdx.x; w < kSlice * 8; w += THREADS) {
+    const int t = w & (kSlice - 1);
+    const int rc = w >> 5;
+    *(u32x4*)(dst + slice_off(t, 64 + rc)) = *(const u32x4*)(raw + t * kFp8RowBytes + kFp8RopeOff + 16 * rc);
+  }
+}
+
 // Dequantise a raw FP8 slice into a bf16 slice (all THREADS threads).
 template <int THREADS>
 __device__ __forceinline__ void dequant_slice(const uint8_t* raw, uint8_t* dst) {
@@ -197,6 +238,12 @@ __device__ __forceinline__ void dequant_slice(const uint8_t* raw, uint8_t* dst) 
     const int rc = w >> 5;
     *(u32x4*)(dst + slice_off(t, 64 + rc)) = *(const u32x4*)(raw + t * kFp8RowBytes + kFp8RopeOff + 16 * rc);
   }
+}
+
+
+// The four group scales of key t of a raw FP8 slice (group g in element g).
+__device__ __forceinline__ f32x4 fp8_scales(const uint8_t* raw, int t) {
+  return *(const f32x4*)(raw + t * kFp8RowBytes + kFp8ScaleOff);
 }
 
 // The schedule's header does not match the call (built for another part or

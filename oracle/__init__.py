@@ -50,7 +50,7 @@ def _load():
         P = ctypes.c_void_p
         i = ctypes.c_int
         lib.oracle_mla_decode.argtypes = [P, P, i, i, P, i, P, P, i, i, i, i,
-                                          ctypes.c_float, i, i, P, P, P, i]
+                                          ctypes.c_float, i, i, P, P, P, i, P]
         lib.oracle_mla_decode.restype = i
         lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_to_double.restype = ctypes.c_double
@@ -88,11 +88,15 @@ def decode_row(row: np.ndarray, fmt: int) -> np.ndarray:
 
 
 def decode_raw(q, kcache, fmt, block_table, seqlens, indices, softmax_scale,
-               causal, sel=None, threads: int = 0):
+               causal, sel=None, threads: int = 0, q_f64=None):
     """out [n, 512] fp64 and lse [n] fp64 for the selected flat query rows
-    ((b*s_q + s)*h_q + h), or for all rows in order."""
+    ((b*s_q + s)*h_q + h), or for all rows in order.  q_f64 (fp64, same
+    shape as q) replaces the bf16 query values when given."""
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.uint16)
+    if q_f64 is not None:
+        q_f64 = np.ascontiguousarray(q_f64, dtype=np.float64)
+        assert q_f64.shape == q.shape
     kcache = np.ascontiguousarray(kcache, dtype=np.uint8)
     block_table = np.ascontiguousarray(block_table, dtype=np.int32)
     seqlens = np.ascontiguousarray(seqlens, dtype=np.int32)
@@ -113,17 +117,18 @@ def decode_raw(q, kcache, fmt, block_table, seqlens, indices, softmax_scale,
                                _ptr(indices), int(topk), int(batch), int(s_q), int(h_q),
                                ctypes.c_float(softmax_scale), int(bool(causal)),
                                int(n if sel is not None else 0), _ptr(sel),
-                               _ptr(out), _ptr(lse), int(threads))
+                               _ptr(out), _ptr(lse), int(threads), _ptr(q_f64))
     if st != 0:
         raise ValueError(f"oracle_mla_decode failed with status {st}")
     return out, lse
 
 
-def decode(inp, sel=None, threads: int = 0):
-    """Run the oracle on an mla_inputs.Inputs bundle."""
+def decode(inp, sel=None, threads: int = 0, q_f64=None):
+    """Run the oracle on an mla_inputs.Inputs bundle (with q_f64 in place
+    of its query values when given)."""
     return decode_raw(inp.q, inp.kcache, inp.fmt, inp.block_table, inp.seqlens,
                       inp.indices, inp.softmax_scale, inp.causal, sel=sel,
-                      threads=threads)
+                      threads=threads, q_f64=q_f64)
 
 
 def merge_partials(lse_parts, o_parts):

@@ -139,6 +139,9 @@ void oracle_decode_row(const uint8_t *row, int fmt, double *dst)
  *   sel          NULL = every row in order; else n_sel flat row ids
  *                ((b * s_q + s) * h_q + h)
  *   out          [n_rows, 512] fp64, lse [n_rows] fp64
+ *   q_f64        NULL, or the query as fp64 values [batch, s_q, h_q, 576]
+ *                used in place of q (e.g. a quantised query that is not a
+ *                bf16 value)
  *
  * Returns 0, or -1 if a needed block_table entry is outside [0, num_pages),
  * -2 on a bad argument, -3 if memory runs out.
@@ -147,9 +150,9 @@ int oracle_mla_decode(const uint16_t *q, const uint8_t *kcache, int fmt, int num
                       const int32_t *block_table, int max_blocks, const int32_t *seqlens,
                       const int32_t *indices, int topk, int batch, int s_q, int h_q,
                       float softmax_scale, int causal, int n_sel, const int32_t *sel,
-                      double *out, double *lse, int num_threads)
+                      double *out, double *lse, int num_threads, const double *q_f64)
 {
-    if (!q || !kcache || !block_table || !seqlens || !out || !lse)
+    if ((!q && !q_f64) || !kcache || !block_table || !seqlens || !out || !lse)
         return -2;
     if (fmt != 0 && fmt != 1)
         return -2;
@@ -222,9 +225,14 @@ int oracle_mla_decode(const uint16_t *q, const uint8_t *kcache, int fmt, int num
                     lse[i] = -INFINITY;
                     continue;
                 }
-                const uint16_t *qp = q + flat * ORC_DQK;
-                for (int d = 0; d < ORC_DQK; ++d)
-                    qrow[d] = oracle_bf16_to_double(qp[d]);
+                if (q_f64) {
+                    for (int d = 0; d < ORC_DQK; ++d)
+                        qrow[d] = q_f64[flat * ORC_DQK + d];
+                } else {
+                    const uint16_t *qp = q + flat * ORC_DQK;
+                    for (int d = 0; d < ORC_DQK; ++d)
+                        qrow[d] = oracle_bf16_to_double(qp[d]);
+                }
                 /* pass 1: every score */
                 int bad = 0;
                 for (int k = 0; k < n; ++k) {

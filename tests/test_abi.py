@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert lib.mla_version() == 1
+    assert lib.mla_version() == 2
 
 
 def test_metadata_size_for_parts(lib):
@@ -189,3 +189,18 @@ def test_python_decode_signature_follows_the_boundary():
     for n in ("softmax_scale", "indices", "metadata"):
         assert sig.parameters[n].default is None
     assert sig.parameters["causal"].default is False
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qk_fp8=1), -2),                                  # bf16 pool
+    (dict(qk_fp8=1, kv_format=1), -2),                     # 16 query rows: the 16-row kernel
+    (dict(qk_fp8=1, kv_format=1, h_q=128), 0),             # FP8, 128 rows per unit
+    (dict(qk_fp8=1, kv_format=1, h_q=16, s_q=4), 0),       # 64 rows per unit
+    (dict(qk_fp8=2, kv_format=1, h_q=128), -1),
+])
+def test_fp8_query_option_needs_fp8_pool_and_wide_units(lib, kw, code):
+    n = ctypes.c_size_t()
+    a = _args(**kw)
+    assert lib.mla_workspace_size(ctypes.byref(a), ctypes.byref(n)) == code
+    if code:
+        assert b"qk_fp8" in lib.mla_last_error()
