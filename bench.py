@@ -97,7 +97,10 @@ class Workload:
         import mla_inputs as gen
         import mla_paged_kv_metadata_amd as m
         self.name = name
-        self.cfg = gen.WORKLOADS[name]
+        # "<workload>_qk8": the same inputs decoded with the query quantised
+        # to e4m3 (qk_fp8, the FP8-MFMA variant)
+        self.qk8 = name.endswith("_qk8")
+        self.cfg = gen.WORKLOADS[name[:-4] if self.qk8 else name]
         t0 = time.time()
         self.inp = gen.make_inputs(self.cfg)
         log(f"[bench] {self.cfg.name}: inputs generated in {time.time() - t0:.1f}s "
@@ -122,7 +125,8 @@ class Workload:
                 k = torch.from_numpy(v.kcache).to(dev)
             bt = torch.from_numpy(v.block_table).to(dev)
             c = m.DecodeCall(self.q, k, bt, self.seqlens, self.mds[r], softmax_scale=inp.softmax_scale,
-                             causal=inp.causal, indices=self.indices, out=out, lse=lse, workspace=ws)
+                             causal=inp.causal, indices=self.indices, out=out, lse=lse, workspace=ws,
+                             qk_fp8=self.qk8)
             out, lse, ws = c.out, c.lse, c.workspace
             self.calls.append(c)
         torch.cuda.synchronize()
@@ -375,9 +379,11 @@ def cpu_tiny_one_thread() -> dict:
 KERNEL_NAMES = {
     "membound": "void mla::narrow::narrow_kernel<0, false>(mla::DecodeParams)",
     "mtp": "mla::wide::offset_kernel(mla::DecodeParams)",
-    "fp8": "void mla::wide::wide_kernel<1, false>(mla::DecodeParams)",
-    "sparse": "void mla::wide::wide_kernel<1, true>(mla::DecodeParams)",
-    "sparse_prefill": "void mla::wide::wide_kernel<1, true>(mla::DecodeParams)",
+    "fp8": "void mla::wide::wide_kernel<1, false, true>(mla::DecodeParams)",
+    "sparse": "void mla::wide::wide_kernel<1, true, true>(mla::DecodeParams)",
+    "fp8_qk8": "void mla::wide::wide_kernel<1, false, false>(mla::DecodeParams)",
+    "sparse_qk8": "void mla::wide::wide_kernel<1, true, false>(mla::DecodeParams)",
+    "sparse_prefill": "void mla::wide::wide_kernel<1, true, true>(mla::DecodeParams)",
     "dense_prefill": "mla::wide::offset_kernel(mla::DecodeParams)",
 }
 KERNEL_SOURCES = {
@@ -385,6 +391,8 @@ KERNEL_SOURCES = {
     "mtp": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
     "fp8": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
     "sparse": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+    "fp8_qk8": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
+    "sparse_qk8": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
     "sparse_prefill": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
     "dense_prefill": ["mla_decode_wide.hip", "mla_slice.h", "mla_device.h", "mla_internal.h"],
 }
@@ -395,6 +403,8 @@ PROFILE_STEM = {
     "mtp": "offset_kernel_mtp_b128_sq2_h128",
     "fp8": "wide_kernel_fp8_b64_h128_L8192",
     "sparse": "wide_kernel_sparse_b32_h128_top2048",
+    "fp8_qk8": "wide_kernel_qk8_fp8_b64_h128_L8192",
+    "sparse_qk8": "wide_kernel_qk8_sparse_b32_h128_top2048",
     "sparse_prefill": "wide_kernel_sparse_prefill_sq2048_h128_top2048",
     "dense_prefill": "offset_kernel_dense_prefill_sq2048_h128_L8192",
 }
@@ -520,11 +530,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true",
                     help="skip every workload but the memory-bound one")
-    ap.add_argument("--only", choices=["membound", "mtp", "fp8", "sparse", "sparse_prefill", "dense_prefill",
-                                       "append"], default=None,
+    ap.add_argument("--only", choices=["membound", "mtp", "fp8", "sparse", "fp8_qk8", "sparse_qk8",
+                                       "sparse_prefill", "dense_prefill", "append"], default=None,
                     help="time just this workload (for profiling)")
     ap.add_argument("--pmc-run", nargs="?", const="membound", default=None,
-                    choices=["membound", "mtp", "fp8", "sparse", "sparse_prefill", "dense_prefill"],
+                    choices=["membound", "mtp", "fp8", "sparse", "fp8_qk8", "sparse_qk8", "sparse_prefill",
+                             "dense_prefill"],
                     help="the run hardware counters are collected on (no timing)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -584,7 +595,7 @@ def main():
     }
     if not args.only_primary:
         extra = {}
-        for key in ("mtp", "fp8", "sparse", "sparse_prefill", "dense_prefill"):
+        for key in ("mtp", "fp8", "sparse", "fp8_qk8", "sparse_qk8", "sparse_prefill", "dense_prefill"):
             del prim
             torch.cuda.empty_cache()
             log(f"[bench] timing {key}")
