@@ -269,11 +269,12 @@ __device__ __forceinline__ void fp8_scale_table(uint8_t* raw, float* scl) {
 // The query of one unit for the fp8 path: lane l holds row row_base + l % 32
 // and, for MFMA m = 0..3, NoPE dims 256 hf + 64 m + 32 (l / 32) .. + 31 in
 // qh[m] (and ql[m]) as 32 e4m3 bytes; the RoPE k-steps j = 0, 1 (dims
-// 512 + 32 hf + 16 j + 8 (l / 32) .. + 7) in qr[j] as bf16; *qsc = 2^p.
+// 512 + 32 hf + 16 j + 8 (l / 32) .. + 7) as bf16 in the wave's LDS area
+// (1 KiB each, lane-major); *qsc = 2^p (times alpha without QLO).
 // Rows past R are zero (p = 0).  A negative softmax scale negates q.
 template <bool QLO>
 __device__ __forceinline__ void load_q_fp8(const DecodeParams& p, int u, int row_base, int hf, bool qneg,
-                                           i32x8 (&qh)[4], i32x8 (&ql)[QLO ? 4 : 1], bf16x8 (&qr)[2],
+                                           i32x8 (&qh)[4], i32x8 (&ql)[QLO ? 4 : 1], uint8_t* qs_mine,
                                            float* qsc) {
   const int lane = opaque_lane();
   const int my_row = row_base + (lane & 31);
@@ -290,9 +291,9 @@ __device__ __forceinline__ void load_q_fp8(const DecodeParams& p, int u, int row
       v[m][k] = row_ok ? (x ^ neg) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 2; ++j) {   // RoPE k-steps to the wave's LDS area
     u32x4 x = *(const u32x4*)(qrow + 2 * (512 + 32 * hf + 16 * j + 8 * hh));
-    qr[j] = __builtin_bit_cast(bf16x8, row_ok ? (x ^ neg) : u32x4{0u, 0u, 0u, 0u});
+    *(u32x4*)(qs_mine + (j * 64 + lane) * 16) = row_ok ? (x ^ neg) : u32x4{0u, 0u, 0u, 0u};
   }
   // Largest magnitude over the row's 256 dims of this half (both lanes of
   // the row), as bf16 bit patterns without sign.
@@ -365,7 +366,7 @@ __device__ __forceinline__ void load_q_fp8(const DecodeParams& p, int u, int row
 template <bool QLO>
 __device__ __forceinline__ f32x16 qk_fp8(const uint8_t* raw, const uint8_t* kb, const float* scl,
                                          const i32x8 (&qh)[4], const i32x8 (&ql)[QLO ? 4 : 1],
-                                         const bf16x8 (&qr)[2], float qsc, int hf) {
+                                         const uint8_t* qs_mine, float qsc, int hf) {
   const int ln = opaque_lane();
   const int t = ln & 31;
   const int hh = ln >> 5;
@@ -389,6 +390,8 @@ __device__ __forceinline__ f32x16 qk_fp8(const uint8_t* raw, const uint8_t* kb, 
     const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
     s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qh[m], s, 0, 0, 0, 127, 0, 127);
     if constexpr (QLO) s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, ql[QLO ? m : 0], s, 0, 0, 0, 127, 0, 123);
+    // one A operand (8 registers) in flight at a time
+    asm volatile("" ::: "memory");
   }
   {
     const float* sB = scl + kSlice * (2 * hf + 1) + 4 * hh;
@@ -403,7 +406,8 @@ __device__ __forceinline__ f32x16 qk_fp8(const uint8_t* raw, const uint8_t* kb, 
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const bf16x8 a = *(const bf16x8*)(kb + 8 * kGroupBytes + t * 128 + 16 * (((4 * hf + 2 * j + hh) ^ sw) & 7));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[j], s, 0, 0, 0);
+    const bf16x8 b = *(const bf16x8*)(qs_mine + (j * 64 + ln) * 16);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
   }
   return s;
 }
@@ -626,7 +630,7 @@ __device__ __forceinline__ bool decode_item(const DecodeParams& p, Item& it) {
 template <int FMT, bool SPARSE, bool QLO = true>
 __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p) {
   using G = Geo<FMT>;
-  constexpr int QL = FMT == 1 ? 1 : G::QL;   // FP8: the whole query in registers
+  constexpr int QL = FMT == 1 ? 2 : G::QL;   // FP8: the RoPE query in LDS, the rest in registers
   constexpr int QR = FMT == 1 ? 1 : kKSteps - QL;
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[G::kRingBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[G::kRingBytes];
@@ -673,10 +677,9 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
     if (SPARSE) fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
     bf16x8 qf[QR];
     i32x8 qh[FMT == 1 ? 4 : 1], ql[FMT == 1 && QLO ? 4 : 1];
-    bf16x8 qr[2];
     float qsc = 1.f;
     if constexpr (FMT == 1)
-      load_q_fp8<QLO>(p, u, row_base, hf, qneg, qh, ql, qr, &qsc);
+      load_q_fp8<QLO>(p, u, row_base, hf, qneg, qh, ql, qs_mine, &qsc);
     else
       load_q(p, u, row_base, hf, qneg, qf, qs_mine);
     wait_vmem<0>();
@@ -731,7 +734,7 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
         fp8_scale_table(rcur, scl);
         lds_barrier();
         kb = kbf;
-        s = qk_fp8<QLO>(rcur, kb, scl, qh, ql, qr, qsc, hf);
+        s = qk_fp8<QLO>(rcur, kb, scl, qh, ql, qs_mine, qsc, hf);
       } else {
         s = qk_partial<QR>(kb, qf, qs_mine, hf);
       }
