@@ -34,7 +34,14 @@ Every graph's output is checked bit for bit against an eager call first.
 `roofline.traffic` (measured HBM bytes per launch) is read from the
 committed counter summary in profiles/ when it was taken on the kernel
 sources as they are now, else null.  `sclk_mhz` is the shader clock sampled
-while the MTP graphs run.
+while the MTP graphs run; `hbm_copy_gbs` is the rate of a plain 1 GiB
+device copy (read + write bytes over time), the streaming rate a simple
+kernel reaches on this part.
+
+    python bench.py --only WORKLOAD --graph-only
+
+times one workload from graph replays only: the run the kernel traces in
+profiles/ are taken on.
 
     python bench.py --pmc-run [membound|mtp|fp8|sparse|...]
 
@@ -471,13 +478,38 @@ def pmc_run(which: str):
     log(f"[bench] pmc run done: 6 calls of {w.cfg.name} ({w.flops} flops, {w.bytes['total']} B per call)")
 
 
-def run_workload(name: str, replicas: int, steps: int, warmup: int):
+def run_workload(name: str, replicas: int, steps: int, warmup: int, graph_only: bool = False):
     w = Workload(name, replicas)
     w.capture()
     w.check_graphs()
     t = {"decode": w.time_graph(w.g_decode, steps), "step_with_schedule": w.time_graph(w.g_step, steps),
-         "dominant_kernel": w.time_graph(w.g_dominant, steps), "eager": w.time_eager(max(5, steps // 4), warmup)}
+         "dominant_kernel": w.time_graph(w.g_dominant, steps)}
+    if not graph_only:
+        t["eager"] = w.time_eager(max(5, steps // 4), warmup)
     return w, t
+
+
+def copy_rate(reps: int = 10) -> float:
+    """HBM rate of a plain device copy (1 GiB read + 1 GiB written per
+    copy, torch's copy kernel), GB/s over `reps` back-to-back copies timed
+    with HIP events: what a simple streaming kernel reaches on this part."""
+    import torch
+    n = 256 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    rate = 2 * n * 4 * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(rate, 1)
 
 
 def roofline_object(w, t, bound: str) -> dict:
@@ -511,7 +543,7 @@ def summary(w, t) -> dict:
         "step_with_schedule_ms": {k: round(v, 5) for k, v in t["step_with_schedule"].items()},
         "dominant_kernel": KERNEL_NAMES[w.name],
         "dominant_kernel_ms": {k: round(v, 5) for k, v in t["dominant_kernel"].items()},
-        "eager_ms": {k: round(v, 5) for k, v in t["eager"].items()},
+        "eager_ms": {k: round(v, 5) for k, v in t["eager"].items()} if "eager" in t else None,
         "tflops": round(w.flops / dec / 1e12, 2),
         "kv_gbs": round(w.bytes["kv"] / dec / 1e9, 1),
         "flops": w.flops,
@@ -533,6 +565,9 @@ def main():
     ap.add_argument("--only", choices=["membound", "mtp", "fp8", "sparse", "fp8_qk8", "sparse_qk8",
                                        "sparse_prefill", "dense_prefill", "append"], default=None,
                     help="time just this workload (for profiling)")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="with --only: time the graph replays only (no eager steps), so that a kernel "
+                         "trace of the run holds graph-ordered launches apart from the set-up calls")
     ap.add_argument("--pmc-run", nargs="?", const="membound", default=None,
                     choices=["membound", "mtp", "fp8", "sparse", "fp8_qk8", "sparse_qk8", "sparse_prefill",
                              "dense_prefill"],
@@ -557,7 +592,7 @@ def main():
         print(json.dumps({"append": bench_append(args.steps)}), flush=True)
         return
     if args.only is not None:
-        w, t = run_workload(args.only, args.replicas, args.steps, args.warmup)
+        w, t = run_workload(args.only, args.replicas, args.steps, args.warmup, args.graph_only)
         print(json.dumps(summary(w, t)), flush=True)
         return
 
@@ -592,6 +627,7 @@ def main():
         "timing_ms": summary(prim, tm),
         "step_with_schedule_kv_gbs": round(kv / (tm["step_with_schedule"]["mean"] * 1e-3) / 1e9, 1),
         "roofline": roofline_object(prim, tm, "hbm"),
+        "hbm_copy_gbs": copy_rate(),
     }
     if not args.only_primary:
         extra = {}

@@ -50,9 +50,10 @@
 //     drain the copies in flight: dense pages come through the scalar cache,
 //     and the pool rows of a sparse unit's index entries are resolved into
 //     an LDS table when the unit starts.
-//   * FP8 slices are copied raw into their own ring and dequantised (e4m3 ->
-//     fp32, times the group scale, -> bf16) into a bf16 slice by all threads
-//     before the MFMA work.
+//   * FP8 slices are copied raw into their own ring.  QK^T reads the raw
+//     e4m3 codes on the fp8 MFMA (below); for PV the slice is dequantised
+//     (e4m3 -> fp32, times the group scale, -> bf16) into a bf16 slice by
+//     all threads.
 //   * Key slots nobody may see are loaded from a visible key of the same
 //     slice (never from outside the sequence) and their probabilities are
 //     forced to zero, so V never carries stale or poisoned memory.
