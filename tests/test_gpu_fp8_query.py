@@ -7,8 +7,8 @@ oracle run on oracle.query_quant.quantize_query(q) at the bf16 bounds, on
 small shapes (poisoned unused slots, dense, causal, sparse with masked and
 out-of-range entries, forced splits) and on sampled rows of the full-size
 FP8 and sparse workloads.  Against the exact oracle (unquantised query) the
-full-size workloads are held to the looser FP8 bound the scope table
-states: |out - ref| <= 2e-2 + 2e-2 |ref|, |lse - ref| <= 5e-3."""
+full-size workloads are held to a looser bound for the quantisation error:
+|out - ref| <= 2e-2 + 2e-2 |ref|, |lse - ref| <= 5e-3."""
 import dataclasses
 
 import numpy as np
