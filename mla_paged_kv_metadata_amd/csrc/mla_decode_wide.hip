@@ -79,7 +79,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // Per-format geometry: ring slot size, copy instructions (64 lanes x 16 B)
 // per slice and per wave, and QL = k-steps of Q kept in LDS instead of
 // VGPRs (LDS: bf16 3 x 36 KiB ring + 32 KiB exchange + 16 KiB Q (+ 4 KiB
-// sparse table) = 160 KiB at most; FP8 3 x 21 KiB ring + 36 KiB slice + 32
+// sparse table) = 160 KiB at most; FP8 3 x 21 KiB ring + 32 KiB V slice + 32
 // + 24 (+ 4) KiB).
 template <int FMT>
 struct Geo {
@@ -201,24 +201,26 @@ __device__ __forceinline__ f32x16 qk_partial(const uint8_t* kb, const bf16x8 (&q
 #pragma unroll
   for (int m = 0; m < 4; ++m)
     ko[m] = t * 128 + (((4 * hf + 2 * m + gg) ^ sw) & 7) * 16 + hf * kGroupBytes * (4 + (m >= 2 ? 1 : 0));
+  // Three fragment reads stay ahead of the MFMA chain.  The order is pinned
+  // with scheduling barriers: left to itself the scheduler moves each read
+  // next to its MFMA when the kernel is near its register limit, and every
+  // MFMA then waits out a whole LDS round trip.
+  auto frag = [&](int ks) -> bf16x8 { return *(const bf16x8*)(kb + ko[ks & 3] + kGroupBytes * (ks >> 2)); };
+  bf16x8 a0 = frag(0), a1 = frag(1), a2 = frag(2);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) {
-    const bf16x8 a = *(const bf16x8*)(kb + ko[ks & 3] + kGroupBytes * (ks >> 2));
     bf16x8 bq;
     if (ks < QR)
       bq = qf[ks < QR ? ks : 0];
     else
       bq = *(const bf16x8*)(qs_mine + ((ks - QR) * 64 + ln) * 16);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq, s, 0, 0, 0);
+    a0 = a1;
+    a1 = a2;
+    if (ks + 3 < kKSteps) a2 = frag(ks + 3);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // Keep three fragment reads ahead of the MFMA chain.
-  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-  for (int i = 0; i < kKSteps - 1; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   return s;
 }
 
@@ -241,8 +243,8 @@ __device__ __forceinline__ f32x16 qk_partial(const uint8_t* kb, const bf16x8 (&q
 // scales of a key are applied to the partial sums (below), so no product
 // code * scale is ever rounded.
 
-// Per-slice scale table, written by the last wave (with 8 waves it has no
-// RoPE copy in dequant_slice): for wave half h and key t, groups 2 h and
+// Per-slice scale table, written by the last wave: for wave half h and key
+// t, groups 2 h and
 // 2 h + 1: scl[32 (2 h) + t] and scl[32 (2 h + 1) + t] the scales, and
 // scl[32 (4 + h) + t] their ratio (v_rcp_f32).  A group whose scale is 0
 // gets its 128 codes zeroed in the raw slice and scale 1, which gives the
@@ -365,9 +367,9 @@ __device__ __forceinline__ void load_q_fp8(const DecodeParams& p, int u, int row
 // (bf16, from the decoded slice kb).  Output register r holds key
 // 8 (r >> 2) + 4 (l / 32) + (r & 3) of the slice for query row l % 32.
 template <bool QLO>
-__device__ __forceinline__ f32x16 qk_fp8(const uint8_t* raw, const uint8_t* kb, const float* scl,
-                                         const i32x8 (&qh)[4], const i32x8 (&ql)[QLO ? 4 : 1],
-                                         const uint8_t* qs_mine, float qsc, int hf) {
+__device__ __forceinline__ f32x16 qk_fp8(const uint8_t* raw, const float* scl, const i32x8 (&qh)[4],
+                                         const i32x8 (&ql)[QLO ? 4 : 1], const uint8_t* qs_mine, float qsc,
+                                         int hf) {
   const int ln = opaque_lane();
   const int t = ln & 31;
   const int hh = ln >> 5;
@@ -375,38 +377,70 @@ __device__ __forceinline__ f32x16 qk_fp8(const uint8_t* raw, const uint8_t* kb, 
   f32x16 s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (m == 2) {   // group A done: s *= scA / scB
-      const float* rA = scl + kSlice * (4 + hf) + 4 * hh;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 r4 = *(const f32x4*)(rA + 8 * j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[4 * j + i] *= r4[i];
-      }
-    }
+  auto frag = [&](int m) -> i32x8 {
     const u32x4 a0 = *(const u32x4*)(krow + 64 * m);
     const u32x4 a1 = *(const u32x4*)(krow + 64 * m + 16);
-    const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-    s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qh[m], s, 0, 0, 0, 127, 0, 127);
-    if constexpr (QLO) s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, ql[QLO ? m : 0], s, 0, 0, 0, 127, 0, 123);
-    // one A operand (8 registers) in flight at a time
-    asm volatile("" ::: "memory");
-  }
-  {
-    const float* sB = scl + kSlice * (2 * hf + 1) + 4 * hh;
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  const float* rA = scl + kSlice * (4 + hf) + 4 * hh;
+  const float* sB = scl + kSlice * (2 * hf + 1) + 4 * hh;
+  if constexpr (QLO) {
+    // Two MFMAs per A operand; one A operand (8 registers) in flight at a
+    // time: this variant has no registers to spare for more.
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m == 2) {   // group A done: s *= scA / scB
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 r4 = *(const f32x4*)(rA + 8 * j);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[4 * j + i] *= r4[i];
+        }
+      }
+      const i32x8 a = frag(m);
+      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qh[m], s, 0, 0, 0, 127, 0, 127);
+      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, ql[QLO ? m : 0], s, 0, 0, 0, 127, 0, 123);
+      asm volatile("" ::: "memory");
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f32x4 b4 = *(const f32x4*)(sB + 8 * j);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[4 * j + i] *= b4[i] * qsc;
     }
+  } else {
+    // One MFMA per A operand: the next A operand is read while the current
+    // one's MFMA runs, and each fold's scales while the MFMA before it runs
+    // (order pinned by scheduling barriers).
+    i32x8 acur = frag(0);
+    f32x4 sc4[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m == 2) {   // group A done: s *= scA / scB
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[4 * j + i] *= sc4[j][i];
+      }
+      const i32x8 a = acur;
+      if (m < 3) acur = frag(m + 1);
+      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qh[m], s, 0, 0, 0, 127, 0, 127);
+      if (m == 1 || m == 3) {
+        const float* src = m == 1 ? rA : sB;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc4[j] = *(const f32x4*)(src + 8 * j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[4 * j + i] *= sc4[j][i] * qsc;
   }
-  const int sw = swz(t);
+  // RoPE dims 512 + 32 hf + 16 j + 8 hh .. + 7, bf16 as stored in the raw row.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const bf16x8 a = *(const bf16x8*)(kb + 8 * kGroupBytes + t * 128 + 16 * (((4 * hf + 2 * j + hh) ^ sw) & 7));
+    const bf16x8 a = *(const bf16x8*)(raw + t * kFp8RowBytes + kFp8RopeOff + 2 * (32 * hf + 16 * j + 8 * hh));
     const bf16x8 b = *(const bf16x8*)(qs_mine + (j * 64 + ln) * 16);
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
   }
@@ -636,7 +670,10 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[G::kRingBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[G::kRingBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[G::kRingBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t kbf[FMT == 1 ? kSliceBytes : 16];
+  // FP8: the slice's V dims (512) dequantised to bf16, chunk groups 0-7 of
+  // the slice layout (the RoPE group is read from the raw rows).
+  __shared__ __attribute__((aligned(1024))) uint8_t kbf[FMT == 1 ? 8 * kGroupBytes : 16];
+  static_assert(kSlice * 32 / kThreads == 2, "two dequantisation items per thread and slice");
   __shared__ __attribute__((aligned(1024))) uint8_t xs[kWaves * kXchgBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t qs[kWaves * QL * 1024];
   __shared__ int32_t tab[SPARSE ? kTab : 1];
@@ -731,11 +768,24 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
       const uint8_t* kb = rcur;
       f32x16 s;
       if constexpr (FMT == 1) {
-        dequant_slice<kThreads>(rcur, kbf);   // V and RoPE, scaled bf16
+        // QK^T reads the raw slice; V is dequantised into kbf (scaled
+        // bf16).  Dequantising after QK^T (published by the exchange barrier
+        // below) lets each wave start its MFMAs one dequantisation earlier;
+        // the exact sparse variant keeps the dequantisation first, where the
+        // other order spills more registers (measured slower).
+        constexpr bool kDequantFirst = SPARSE && QLO;
+        if constexpr (kDequantFirst) {
+#pragma unroll 1
+          for (int i = 0; i < 2; ++i) dequant_item<kThreads>(rcur, kbf, i);
+        }
         fp8_scale_table(rcur, scl);
         lds_barrier();
+        s = qk_fp8<QLO>(rcur, scl, qh, ql, qs_mine, qsc, hf);
+        if constexpr (!kDequantFirst) {
+          dequant_item<kThreads>(rcur, kbf, 0);
+          dequant_item<kThreads>(rcur, kbf, 1);
+        }
         kb = kbf;
-        s = qk_fp8<QLO>(rcur, kb, scl, qh, ql, qs_mine, qsc, hf);
       } else {
         s = qk_partial<QR>(kb, qf, qs_mine, hf);
       }
