@@ -285,18 +285,22 @@ __device__ __forceinline__ void load_q_fp8(const DecodeParams& p, int u, int row
   const int hh = lane >> 5;
   const uint8_t* qrow = p.q + ((size_t)u * p.R + (row_ok ? my_row : 0)) * (2 * kDqk);
   const uint32_t neg = qneg ? 0x80008000u : 0u;
+  // Rows past R read row 0 (in bounds) and are zeroed with a mask.  A select
+  // on the loaded value would be turned into a branch around each load, and
+  // the 18 loads would then wait out their memory round trips one by one.
+  const uint32_t keep = row_ok ? 0xFFFFFFFFu : 0u;
   u32x4 v[4][4];   // [m][16-byte part]: 8 bf16 each
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      u32x4 x = *(const u32x4*)(qrow + 2 * (256 * hf + 64 * m + 32 * hh) + 16 * k);
-      v[m][k] = row_ok ? (x ^ neg) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 x = *(const u32x4*)(qrow + 2 * (256 * hf + 64 * m + 32 * hh) + 16 * k);
+      v[m][k] = (x ^ neg) & keep;
     }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {   // RoPE k-steps to the wave's LDS area
-    u32x4 x = *(const u32x4*)(qrow + 2 * (512 + 32 * hf + 16 * j + 8 * hh));
-    *(u32x4*)(qs_mine + (j * 64 + lane) * 16) = row_ok ? (x ^ neg) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 x = *(const u32x4*)(qrow + 2 * (512 + 32 * hf + 16 * j + 8 * hh));
+    *(u32x4*)(qs_mine + (j * 64 + lane) * 16) = (x ^ neg) & keep;
   }
   // Largest magnitude over the row's 256 dims of this half (both lanes of
   // the row), as bf16 bit patterns without sign.
@@ -712,7 +716,13 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
     const int s_end = 2 * je;
     const int pos_end = kPage * je;   // sparse: index entries, resolved kTab at a time
     int tab_base = kPage * jb;
-    if (SPARSE) fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
+    // Sparse: the index entries are loaded first, and the query loads go
+    // out behind them (one round trip for both); the block-table lookups
+    // follow once the query is in registers.
+    static_assert(kTab <= 2 * kThreads, "two table entries per thread");
+    const int tab_count = SPARSE ? min(pos_end - tab_base, kTab) : 0;
+    int2 tix = make_int2(-1, -1);
+    if (SPARSE) tix = fill_table_issue<kThreads>(p, tab_base, tab_count, idx_row);
     bf16x8 qf[QR];
     i32x8 qh[FMT == 1 ? 4 : 1], ql[FMT == 1 && QLO ? 4 : 1];
     float qsc = 1.f;
@@ -720,6 +730,7 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
       load_q_fp8<QLO>(p, u, row_base, hf, qneg, qh, ql, qs_mine, &qsc);
     else
       load_q(p, u, row_base, hf, qneg, qf, qs_mine);
+    if (SPARSE) fill_table_finish<kThreads>(p, tab, b, tab_count, Wunit, tix);
     wait_vmem<0>();
     lds_barrier();   // tab complete
 

@@ -107,6 +107,31 @@ __device__ __forceinline__ void fill_table(const DecodeParams& p, int32_t* tab, 
   }
 }
 
+// The same fill in two halves, for a table of at most 2 THREADS entries:
+// fill_table_issue loads the thread's index entries (a unit's start issues
+// its query loads right after them, so both share one round trip);
+// fill_table_finish resolves them through the block table and writes tab.
+template <int THREADS>
+__device__ __forceinline__ int2 fill_table_issue(const DecodeParams& p, int base, int count,
+                                                 const int32_t* idx_row) {
+  int2 t = make_int2(-1, -1);
+  const int i0 = threadIdx.x, i1 = threadIdx.x + THREADS;
+  if (i0 < count && base + i0 < p.topk) t.x = idx_row[base + i0];
+  if (i1 < count && base + i1 < p.topk) t.y = idx_row[base + i1];
+  return t;
+}
+template <int THREADS>
+__device__ __forceinline__ void fill_table_finish(const DecodeParams& p, int32_t* tab, int b, int count, int Wunit,
+                                                  int2 t) {
+  const int i0 = threadIdx.x, i1 = threadIdx.x + THREADS;
+  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
+  int v0 = -1, v1 = -1;
+  if (t.x >= 0 && t.x < Wunit) v0 = bt[t.x >> 6] * kPage + (t.x & (kPage - 1));
+  if (t.y >= 0 && t.y < Wunit) v1 = bt[t.y >> 6] * kPage + (t.y & (kPage - 1));
+  if (i0 < count) tab[i0] = v0;
+  if (i1 < count) tab[i1] = v1;
+}
+
 // Dense: the page of block j of sequence b (0 past the end of the
 // sequence), read through the scalar cache.  Scalar loads are counted by
 // lgkmcnt, so waiting for one leaves the copies into LDS in flight.
