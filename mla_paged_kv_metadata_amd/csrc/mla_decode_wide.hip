@@ -642,23 +642,36 @@ __device__ __forceinline__ int causal_tile_end(const DecodeParams& p, int rt, in
 // go to different XCDs, the row tiles of one part share an XCD and its L2).
 struct Item {
   int part, rt, u0, j0, u1, j1, split0;
+  int L0, n0;   // length and block count of the first unit (from the part row)
   const int32_t* unit_blocks;
 };
 // A schedule header that does not match the call gives every row out = 0
 // and lse = NaN (fill_mismatch) and no work item.
+// A uniform int32 the kernel never writes, through the scalar cache (waited
+// for by lgkmcnt, so vector-memory waits do not cover it and it does not
+// hold up the copies in flight).
+__device__ __forceinline__ int scalar_ld(const int32_t* base, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)base)[i];
+}
+
+// The header and the part row are read together (one round trip);
+// workgroups past the last part read the last part's row and then stop.
 __device__ __forceinline__ bool decode_item(const DecodeParams& p, Item& it) {
   work_item(blockIdx.x, p.num_parts, p.row_tiles, &it.part, &it.rt);
-  if (!header_ok(p, p.md[0], p.md[3], p.md[5])) {
-    fill_mismatch<kThreads>(p);
-    return false;
-  }
-  if (it.part >= p.num_parts) return false;
-  const int32_t* prow = p.md + kHeader + kPartRow * it.part;
+  const int32_t* prow = p.md + kHeader + kPartRow * min(it.part, p.num_parts - 1);
+  const int h0 = p.md[0], h3 = p.md[3], h5 = p.md[5];
   it.u0 = prow[0];
   it.j0 = prow[1];
   it.u1 = prow[2];
   it.j1 = prow[3];
   it.split0 = prow[4];
+  it.L0 = prow[5];
+  it.n0 = prow[6];
+  if (!header_ok(p, h0, h3, h5)) {
+    fill_mismatch<kThreads>(p);
+    return false;
+  }
+  if (it.part >= p.num_parts) return false;
   it.unit_blocks = p.md + kHeader + kPartRow * p.num_parts;
   return it.u0 >= 0;
 }
@@ -700,11 +713,19 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
   const float sc = fabsf(p.scale_log2);
   const bool qneg = p.scale_log2 < 0.f;
 
+  // Length and block count of the current unit: the part row carries them
+  // for the first unit; those of the next are loaded at each unit start and
+  // waited for with the unit's own loads.
+  int L_nx = it.L0, n_nx = it.n0;
   for (int u = it.u0; u <= it.u1; ++u) {
     const int jb = (u == it.u0) ? it.j0 : 0;
-    const int je_part = (u == it.u1) ? it.j1 : it.unit_blocks[u];
+    const int je_part = (u == it.u1) ? it.j1 : n_nx;
     const int b = SPARSE ? u / p.s_q : u;
-    const int L = p.seqlens[b];
+    const int L = L_nx;
+    if (u < it.u1) {
+      n_nx = scalar_ld(it.unit_blocks, u + 1);
+      L_nx = scalar_ld(p.seqlens, SPARSE ? (u + 1) / p.s_q : u + 1);
+    }
     const int je = (SPARSE || !p.causal) ? je_part : causal_tile_end(p, it.rt, L, jb, je_part);
     const int s_unit = SPARSE ? u % p.s_q : 0;
     const int s_row = SPARSE ? s_unit : (row_ok ? my_row / p.h_q : 0);
@@ -858,11 +879,16 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
   const float sc = fabsf(p.scale_log2);
   const bool qneg = p.scale_log2 < 0.f;
 
+  int L_nx = it.L0, n_nx = it.n0;   // as in wide_kernel
   for (int u = it.u0; u <= it.u1; ++u) {
     const int jb = (u == it.u0) ? it.j0 : 0;
-    const int je_part = (u == it.u1) ? it.j1 : it.unit_blocks[u];
+    const int je_part = (u == it.u1) ? it.j1 : n_nx;
     const int b = u;
-    const int L = p.seqlens[b];
+    const int L = L_nx;
+    if (u < it.u1) {
+      n_nx = scalar_ld(it.unit_blocks, u + 1);
+      L_nx = scalar_ld(p.seqlens, u + 1);
+    }
     const int je = p.causal ? causal_tile_end(p, it.rt, L, jb, je_part) : je_part;
     const int s_row = row_ok ? my_row / p.h_q : 0;
     const int W = p.causal ? min(max(L - p.s_q + 1 + s_row, 0), L) : L;
