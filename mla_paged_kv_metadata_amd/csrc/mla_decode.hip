@@ -82,14 +82,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse, int R, int num_parts,
                                                       int units) {
-  // A schedule that does not match the call: the split-KV kernel has
-  // already given every row out = 0 and lse = NaN; nothing to merge.
-  if (md[0] != num_parts || md[5] != kMagic || md[3] != units) return;
   // Workgroup = (unit, four rows), flattened so that any row count fits.
   const int quads = (R + 3) / 4;
   const int u = blockIdx.x / quads;
+  // The header and the unit's split range are read together (one round
+  // trip; the checks below do not short-circuit the loads).
+  const int h0 = md[0], h3 = md[3], h5 = md[5];
   const int base = num_splits[u];
   const int k = num_splits[u + 1] - base;
+  // A schedule that does not match the call: the split-KV kernel has
+  // already given every row out = 0 and lse = NaN; nothing to merge.
+  if ((h0 != num_parts) | (h5 != kMagic) | (h3 != units)) return;
   if (k <= 1) return;
   const int lane = threadIdx.x & 63;
   const int r = (blockIdx.x - u * quads) * 4 + (threadIdx.x >> 6);
@@ -100,9 +103,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   constexpr int kPre = 8;
   const uint16_t* src = ws_o + ((size_t)base * R + r) * kDv + 8 * lane;
   const size_t stride = (size_t)R * kDv;
+  // The first kPre partial rows, loaded unconditionally (rows past the
+  // unit's last split repeat that split and get weight 0), so that all of
+  // them are in flight at once.
   u32x4 pre[kPre];
 #pragma unroll
-  for (int j = 0; j < kPre; ++j) pre[j] = j < k ? *(const u32x4*)(src + j * stride) : u32x4{0, 0, 0, 0};
+  for (int j = 0; j < kPre; ++j) pre[j] = *(const u32x4*)(src + (size_t)min(j, k - 1) * stride);
   float M = own;
   for (int i = 64 + lane; i < k; i += 64) M = fmaxf(M, lrow[(size_t)i * R]);
   M = wave_max(M);
