@@ -187,7 +187,10 @@ mla_status mla_workspace_size(const mla_decode_args *args, size_t *bytes);
  * kernels check the schedule's header on the device: if it was built for
  * another part or unit count (or is not a schedule), no key is read and
  * every row gets out = 0 and lse = NaN (the call itself cannot see this
- * and returns MLA_OK; mla_validate_inputs names the problem).
+ * and returns MLA_OK; mla_validate_inputs names the problem).  The header
+ * is read together with the part row of each workgroup, so tile_metadata
+ * must span the tile_metadata_elems that mla_metadata_size gives for this
+ * call's num_parts even when it holds a schedule for fewer parts.
  * Limits (MLA_ERR_INVALID_ARGUMENT beyond them): batch * s_q * h_q below
  * 2^31 query rows, and num_parts (rounded up to a multiple of 8 when >= 8)
  * times the row tiles of one unit below 2^31 workgroups.
