@@ -333,6 +333,18 @@ def bench_append(reps: int) -> dict:
     return out
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), for the oracle's timing line."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, target_s: float, unit: str, threads=None) -> dict:
     """The fp64 oracle on a bounded sample of the same workload: whole
     sequences (all their query rows), taken in order until about target_s of
@@ -360,7 +372,7 @@ def cpu_baseline(inp, target_s: float, unit: str, threads=None) -> dict:
     kv = sub.kv_bytes_read()
     flops = sub.flops()
     value = kv / dt / 1e9 if unit == "GB/s" else flops / dt / 1e12
-    return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
+    return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {nb} of {inp.batch} sequences, all {rows_per_b} query rows each "
                       f"({kv / 1e6:.1f} MB of KV rows, {flops / 1e9:.2f} GFLOP); median of 3 runs "
                       f"({', '.join(f'{t:.2f}' for t in times)} s)",
