@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
         qf[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    if (SPARSE) fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, G::kTabN), Wunit, idx_row);
+    if (SPARSE) fill_table<kThreads, G::kTabN / kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, G::kTabN), Wunit, idx_row);
     // Dense: lane i holds the page of block pb + i.
     int pb = jb;
     int pages_v = 0;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
           const int pos = kPage * (j + 1);
           if (pos + kPage - tab_base > G::kTabN) {   // the unit's range outgrew the table
             tab_base = pos;
-            fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, G::kTabN), Wunit, idx_row);
+            fill_table<kThreads, G::kTabN / kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, G::kTabN), Wunit, idx_row);
             wait_vmem<0>();
             lds_barrier();
           }

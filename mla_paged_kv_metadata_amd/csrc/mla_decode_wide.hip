@@ -367,9 +367,10 @@ __device__ __forceinline__ void load_q_fp8(const DecodeParams& p, int u, int row
 
 // Partial S^T of this wave's half for FP8 pools: NoPE groups A = 2 hf (fp8
 // MFMAs m = 0, 1) and B = 2 hf + 1 (m = 2, 3) in one accumulator,
-// s = ((sum_A * scA / scB) + sum_B) * scB * 2^p, then the two RoPE k-steps
-// (bf16, from the decoded slice kb).  Output register r holds key
-// 8 (r >> 2) + 4 (l / 32) + (r & 3) of the slice for query row l % 32.
+// s = ((sum_A * scA / scB) + sum_B) * scB * qsc (qsc = 2^p, times alpha
+// without the low part), then the two RoPE k-steps (bf16, read from the raw
+// rows as stored).  Output register r holds key 8 (r >> 2) + 4 (l / 32) +
+// (r & 3) of the slice for query row l % 32.
 template <bool QLO>
 __device__ __forceinline__ f32x16 qk_fp8(const uint8_t* raw, const float* scl, const i32x8 (&qh)[4],
                                          const i32x8 (&ql)[QLO ? 4 : 1], const uint8_t* qs_mine, float qsc,
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
         const int pos = kSlice * (sl + 2);
         if (pos - tab_base >= kTab) {   // the unit's range outgrew the table
           tab_base = pos;
-          fill_table<kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
+          fill_table<kThreads, kTab / kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, kTab), Wunit, idx_row);
           lds_barrier();
         }
       }

@@ -94,16 +94,34 @@ __device__ __forceinline__ float xor16(float v) {
 // Sparse: resolve entries base .. base + count - 1 of the unit's index list
 // into tab (all THREADS threads): the pool row of the indexed key, or -1
 // when the entry is out of range or not visible to the unit.
-template <int THREADS>
+// Entries are resolved in three batches, so that a fill costs two memory
+// round trips whatever its size: every index entry is loaded, then every
+// block-table entry (unconditionally: a masked entry reads entry 0 of the
+// sequence's row, always in bounds, and is masked to -1 with bit
+// operations, because a select on a loaded value becomes a branch and a
+// wait around each load), then the table is written.
+__device__ __forceinline__ int resolve_row(int page, int t, bool ok) {
+  return (page * kPage + (t & (kPage - 1))) | (ok ? 0 : -1);
+}
+
+template <int THREADS, int MAXN>
 __device__ __forceinline__ void fill_table(const DecodeParams& p, int32_t* tab, int b, int base, int count,
                                            int Wunit, const int32_t* idx_row) {
-  for (int i = threadIdx.x; i < count; i += THREADS) {
-    const int e = base + i;
-    const int t = e < p.topk ? idx_row[e] : -1;
-    int v = -1;
-    if (t >= 0 && t < Wunit)
-      v = p.block_table[(size_t)b * p.max_blocks + (t >> 6)] * kPage + (t & (kPage - 1));
-    tab[i] = v;
+  int t[MAXN];
+#pragma unroll
+  for (int i = 0; i < MAXN; ++i) {
+    const int k = (int)threadIdx.x + THREADS * i;
+    t[i] = -1;
+    if (k < count && base + k < p.topk) t[i] = idx_row[base + k];
+  }
+  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
+  int pg[MAXN];
+#pragma unroll
+  for (int i = 0; i < MAXN; ++i) pg[i] = bt[(t[i] >= 0 && t[i] < Wunit) ? (t[i] >> 6) : 0];
+#pragma unroll
+  for (int i = 0; i < MAXN; ++i) {
+    const int k = (int)threadIdx.x + THREADS * i;
+    if (k < count) tab[k] = resolve_row(pg[i], t[i], t[i] >= 0 && t[i] < Wunit);
   }
 }
 
@@ -125,11 +143,11 @@ __device__ __forceinline__ void fill_table_finish(const DecodeParams& p, int32_t
                                                   int2 t) {
   const int i0 = threadIdx.x, i1 = threadIdx.x + THREADS;
   const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
-  int v0 = -1, v1 = -1;
-  if (t.x >= 0 && t.x < Wunit) v0 = bt[t.x >> 6] * kPage + (t.x & (kPage - 1));
-  if (t.y >= 0 && t.y < Wunit) v1 = bt[t.y >> 6] * kPage + (t.y & (kPage - 1));
-  if (i0 < count) tab[i0] = v0;
-  if (i1 < count) tab[i1] = v1;
+  const bool ok0 = t.x >= 0 && t.x < Wunit, ok1 = t.y >= 0 && t.y < Wunit;
+  const int pg0 = bt[ok0 ? (t.x >> 6) : 0];
+  const int pg1 = bt[ok1 ? (t.y >> 6) : 0];
+  if (i0 < count) tab[i0] = resolve_row(pg0, t.x, ok0);
+  if (i1 < count) tab[i1] = resolve_row(pg1, t.y, ok1);
 }
 
 // Dense: the page of block j of sequence b (0 past the end of the
