@@ -105,6 +105,9 @@ __device__ __forceinline__ uint64_t copy_page(const DecodeParams& p, const int32
 template <int FMT, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams p) {
   using G = Geo<FMT, SPARSE>;
+  // Copy instructions of one page that every wave issues at least (bf16:
+  // 18 each; FP8: 41 over four waves, at least 10 each).
+  constexpr int kFirstWait = FMT == 0 ? 18 : kRawInst / kWaves;
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[G::kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[G::kSlotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t kbf[FMT == 1 ? kPageBf16 : 16];
@@ -196,8 +199,12 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
       }
       return __builtin_amdgcn_readlane(pages_v, j - pb);
     };
+    // Both slots are free at the unit's start: its first two pages are
+    // requested together, so the second does not wait for the first to land.
     uint64_t vis_cur = copy_page<FMT, SPARSE>(p, tab, tab_base, slot0, jb, L, page_at(jb));
     uint64_t vis_next = 0;
+    const bool two = jb + 1 < je;
+    if (two) vis_next = copy_page<FMT, SPARSE>(p, tab, tab_base, slot1, jb + 1, L, page_at(jb + 1));
 
     float m_run = -INFINITY;
     float l_part = 0.f;
@@ -209,10 +216,16 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
       constexpr int C = decltype(slot_c)::value;
       uint8_t* const rcur = C == 0 ? slot0 : slot1;
       uint8_t* const rnext = C == 0 ? slot1 : slot0;
-      wait_vmem<0>();
+      // Page j must be in LDS.  In the unit's first step the second page's
+      // copies (the last kFirstWait or more of this wave) may still fly.
+      if (j == jb && two)
+        wait_vmem<kFirstWait>();
+      else
+        wait_vmem<0>();
       lds_barrier();   // page j visible; the other slot (page j - 1) free
-      // ---- copy page j + 1 into the other slot.
-      if (j + 1 < je) {
+      // ---- copy page j + 1 into the other slot (already requested in the
+      // unit's first step).
+      if (j + 1 < je && j != jb) {
         if (SPARSE) {
           const int pos = kPage * (j + 1);
           if (pos + kPage - tab_base > G::kTabN) {   // the unit's range outgrew the table
