@@ -13,7 +13,9 @@
 // to hide its latencies behind, so every step is built to be short:
 //   * One workgroup = 4 waves = 16 query rows, one step = one 64-token page.
 //     Pages stream through two LDS page slots filled by global_load_lds (no
-//     VGPR round trip): page p + 1 is in flight while page p is computed.
+//     VGPR round trip).  Page p + 2 is requested as soon as every wave is
+//     done with page p (its slot), so while page p + 1 is awaited two pages
+//     are in flight; a unit's first two pages are requested together.
 //   * QK: wave w computes the full S^T tile of keys 16 w .. 16 w + 15 over
 //     all 576 dims (18 v_mfma_f32_16x16x32_bf16, Q^T kept in registers for
 //     the whole unit), so there are no partial sums to reduce; the four 1 KiB
@@ -23,8 +25,8 @@
 //     B operand P^T of the 16x16x32 PV products (the k order of V^T follows
 //     them), so P never leaves registers; wave w accumulates O^T for V dims
 //     128 w .. 128 w + 127 from ds_read_b64_tr_b16 reads of V^T.
-//   * Two barriers per page: one for the page's arrival (which also frees
-//     the other slot for the next page), one for the S^T exchange.
+//   * Three barriers per page: the page's arrival, the S^T exchange, and
+//     the release of its slot for page p + 2.
 //   * FP8 pages are copied raw and dequantised into one bf16 page by all
 //     threads after the arrival barrier (one more barrier per page).
 //   * Page numbers of a dense unit are held one per lane and read with
@@ -201,10 +203,10 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
     };
     // Both slots are free at the unit's start: its first two pages are
     // requested together, so the second does not wait for the first to land.
-    uint64_t vis_cur = copy_page<FMT, SPARSE>(p, tab, tab_base, slot0, jb, L, page_at(jb));
-    uint64_t vis_next = 0;
-    const bool two = jb + 1 < je;
-    if (two) vis_next = copy_page<FMT, SPARSE>(p, tab, tab_base, slot1, jb + 1, L, page_at(jb + 1));
+    uint64_t vis[2];   // visible-key mask of the page in each slot
+    vis[0] = copy_page<FMT, SPARSE>(p, tab, tab_base, slot0, jb, L, page_at(jb));
+    vis[1] = 0u;
+    if (jb + 1 < je) vis[1] = copy_page<FMT, SPARSE>(p, tab, tab_base, slot1, jb + 1, L, page_at(jb + 1));
 
     float m_run = -INFINITY;
     float l_part = 0.f;
@@ -215,30 +217,15 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
     auto step = [&](auto slot_c, int j) __attribute__((always_inline)) {
       constexpr int C = decltype(slot_c)::value;
       uint8_t* const rcur = C == 0 ? slot0 : slot1;
-      uint8_t* const rnext = C == 0 ? slot1 : slot0;
-      // Page j must be in LDS.  In the unit's first step the second page's
-      // copies (the last kFirstWait or more of this wave) may still fly.
-      if (j == jb && two)
+      // Page j must be in LDS; page j + 1's copies (requested after page
+      // j - 1 was done, or at the unit's start) may still fly: at least
+      // kFirstWait instructions of this wave.
+      if (j + 1 < je)
         wait_vmem<kFirstWait>();
       else
         wait_vmem<0>();
-      lds_barrier();   // page j visible; the other slot (page j - 1) free
-      // ---- copy page j + 1 into the other slot (already requested in the
-      // unit's first step).
-      if (j + 1 < je && j != jb) {
-        if (SPARSE) {
-          const int pos = kPage * (j + 1);
-          if (pos + kPage - tab_base > G::kTabN) {   // the unit's range outgrew the table
-            tab_base = pos;
-            fill_table<kThreads, G::kTabN / kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, G::kTabN), Wunit, idx_row);
-            wait_vmem<0>();
-            lds_barrier();
-          }
-        }
-        vis_next = copy_page<FMT, SPARSE>(p, tab, tab_base, rnext, j + 1, L, page_at(j + 1));
-      }
-      const uint64_t vmask = vis_cur;
-      vis_cur = vis_next;
+      lds_barrier();   // page j visible
+      const uint64_t vmask = vis[C];
       const uint8_t* kb = rcur;
       if constexpr (FMT == 1) {
         if (vmask != 0u) {
@@ -248,143 +235,159 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
         lds_barrier();   // kbf holds page j
         kb = kbf;
       }
-      if (vmask == 0u) return;
-      // ---- S^T tile of keys 16 wave .. + 15 (half wave >> 1 of the page,
-      // keys 16 (wave & 1) + l % 16) over all 18 k-steps.
-      {
-        const uint8_t* kh = kb + (wave >> 1) * kSliceBytes;
-        const int ln = opaque_lane();
-        const int t = 16 * (wave & 1) + (ln & 15);
-        const int gg = ln >> 4;
-        f32x4 sres;
-        if constexpr (FMT == 1) {
-          // Exact codes: k-steps 4 G .. 4 G + 3 are NoPE group G, 16 and 17
-          // RoPE.  Each group's partial sums are multiplied by that group's
-          // scale of their key (the lane's output keys 16 (wave & 1) + 4 g
-          // + i of half wave >> 1: raw rows 32 (wave >> 1) + ...).
-          f32x4 sc4[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sc4[i] = fp8_scales(rcur, 32 * (wave >> 1) + 16 * (wave & 1) + 4 * gg + i);
-          f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f};
-          sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kh + slice_off(t, 64 + gg)), qf[16], sr,
-                                                       0, 0, 0);
-          sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kh + slice_off(t, 68 + gg)), qf[17], sr,
-                                                       0, 0, 0);
-#pragma unroll
-          for (int G = 0; G < 4; ++G) {
-            f32x4 ta = f32x4{0.f, 0.f, 0.f, 0.f}, tb = ta;
-#pragma unroll
-            for (int kk = 0; kk < 4; kk += 2) {
-              const int ks = 4 * G + kk;
+      if (vmask != 0u) {
+        // ---- S^T tile of keys 16 wave .. + 15 (half wave >> 1 of the page,
+        // keys 16 (wave & 1) + l % 16) over all 18 k-steps.
+        {
+          const uint8_t* kh = kb + (wave >> 1) * kSliceBytes;
+          const int ln = opaque_lane();
+          const int t = 16 * (wave & 1) + (ln & 15);
+          const int gg = ln >> 4;
+          f32x4 sres;
+          if constexpr (FMT == 1) {
+            // Exact codes: k-steps 4 G .. 4 G + 3 are NoPE group G, 16 and 17
+            // RoPE.  Each group's partial sums are multiplied by that group's
+            // scale of their key (the lane's output keys 16 (wave & 1) + 4 g
+            // + i of half wave >> 1: raw rows 32 (wave >> 1) + ...).
+            f32x4 sc4[4];
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) sc4[i] = fp8_scales(rcur, 32 * (wave >> 1) + 16 * (wave & 1) + 4 * gg + i);
+            f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f};
+            sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kh + slice_off(t, 64 + gg)), qf[16], sr,
+                                                         0, 0, 0);
+            sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kh + slice_off(t, 68 + gg)), qf[17], sr,
+                                                         0, 0, 0);
+  #pragma unroll
+            for (int G = 0; G < 4; ++G) {
+              f32x4 ta = f32x4{0.f, 0.f, 0.f, 0.f}, tb = ta;
+  #pragma unroll
+              for (int kk = 0; kk < 4; kk += 2) {
+                const int ks = 4 * G + kk;
+                const bf16x8 a0 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + gg));
+                const bf16x8 a1 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + 4 + gg));
+                ta = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], ta, 0, 0, 0);
+                tb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], tb, 0, 0, 0);
+              }
+              const f32x4 tg = ta + tb;
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) sr[i] = __builtin_fmaf(tg[i], sc4[i][G], sr[i]);
+            }
+            sres = sr;
+          } else {
+            f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
+  #pragma unroll
+            for (int ks = 0; ks < kKSteps; ks += 2) {
               const bf16x8 a0 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + gg));
               const bf16x8 a1 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + 4 + gg));
-              ta = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], ta, 0, 0, 0);
-              tb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], tb, 0, 0, 0);
+              sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], sa, 0, 0, 0);
+              sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], sb, 0, 0, 0);
             }
-            const f32x4 tg = ta + tb;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sr[i] = __builtin_fmaf(tg[i], sc4[i][G], sr[i]);
+            sres = sa + sb;
           }
-          sres = sr;
-        } else {
-          f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
-#pragma unroll
-          for (int ks = 0; ks < kKSteps; ks += 2) {
-            const bf16x8 a0 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + gg));
-            const bf16x8 a1 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + 4 + gg));
-            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], sa, 0, 0, 0);
-            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], sb, 0, 0, 0);
+          *(f32x4*)(xs + wave * 1024 + lane * 16) = sres;
+        }
+        lds_barrier();   // all four S^T tiles visible
+        // ---- lane holds row l % 16 and keys 16 w + 4 g + i (i < 4) for w < 4.
+        float sv[16];
+  #pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const f32x4 a = *(const f32x4*)(xs + w * 1024 + lane * 16);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) sv[4 * w + i] = a[i];
+        }
+        // ---- mask + online softmax (exp2 domain, logit = sc * s).
+        const int key0 = kPage * j;
+        const bool full = SPARSE ? (vmask == ~0ull) : (key0 + kPage <= W_lo);
+        uint32_t okbits = 0xFFFFu;
+        if (!full) {
+          okbits = 0u;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int tl = 16 * (i >> 2) + 4 * g + (i & 3);
+            const bool ok = SPARSE ? ((vmask >> tl) & 1u) != 0u : (key0 + tl < W);
+            okbits |= ok ? (1u << i) : 0u;
+            sv[i] = ok ? sv[i] : -INFINITY;
           }
-          sres = sa + sb;
         }
-        *(f32x4*)(xs + wave * 1024 + lane * 16) = sres;
-      }
-      lds_barrier();   // all four S^T tiles visible
-      // ---- lane holds row l % 16 and keys 16 w + 4 g + i (i < 4) for w < 4.
-      float sv[16];
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const f32x4 a = *(const f32x4*)(xs + w * 1024 + lane * 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[4 * w + i] = a[i];
-      }
-      // ---- mask + online softmax (exp2 domain, logit = sc * s).
-      const int key0 = kPage * j;
-      const bool full = SPARSE ? (vmask == ~0ull) : (key0 + kPage <= W_lo);
-      uint32_t okbits = 0xFFFFu;
-      if (!full) {
-        okbits = 0u;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tl = 16 * (i >> 2) + 4 * g + (i & 3);
-          const bool ok = SPARSE ? ((vmask >> tl) & 1u) != 0u : (key0 + tl < W);
-          okbits |= ok ? (1u << i) : 0u;
-          sv[i] = ok ? sv[i] : -INFINITY;
+        float mx = -INFINITY;
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+        mx = fmaxf(mx, xor16(mx));
+        mx = fmaxf(mx, xor32(mx));
+        mx = mx == -INFINITY ? -INFINITY : mx * sc;
+        const bool raise = mx > m_run + kRescaleSlack;
+        if (__any(raise)) {
+          const float m_new = raise ? mx : m_run;
+          const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+          m_run = m_new;
+          l_part *= alpha;
+  #pragma unroll
+          for (int d = 0; d < kDimTiles; ++d) o[d] *= alpha;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float e[16];
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) e[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -m_use));
+        if (!full) {
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) e[i] = ((okbits >> i) & 1u) ? e[i] : 0.f;
+        }
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) l_part += e[i];
+        // ---- O^T += V^T P^T over the two halves of the page.  PV k-step h
+        // covers key tiles 2 h and 2 h + 1: k-slot i of lane group g is key
+        // 4 g + i of tile 2 h (i < 4) or of tile 2 h + 1 (i >= 4); the
+        // transposed read of 16-lane group G takes keys 4 G + (j >> 2) (+ 16
+        // for the second read) and dims 4 (j & 3) .. + 3 of the dim tile, i.e.
+        // chunk 16 wave + 2 dt + ((j >> 1) & 1) of the half.
+  #pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // FP8: wave w's V dims are NoPE group w; the probabilities times
+          // that group's scale of their key (page key 32 h + 16 (i >> 2) +
+          // 4 g + (i & 3) for e[8 h + i]).
+          float ev[8];
+  #pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            ev[i] = e[8 * h + i];
+            if constexpr (FMT == 1)
+              ev[i] *= *(const float*)(rcur + (32 * h + 16 * (i >> 2) + 4 * g + (i & 3)) * kFp8RowBytes +
+                                       kFp8ScaleOff + 4 * wave);
+          }
+          const bf16x8 pb = __builtin_bit_cast(
+              bf16x8, u32x4{pack_bf16x2(ev[0], ev[1]), pack_bf16x2(ev[2], ev[3]), pack_bf16x2(ev[4], ev[5]),
+                            pack_bf16x2(ev[6], ev[7])});
+          const uint8_t* vh = kb + h * kSliceBytes;
+          const int ln = opaque_lane();
+          const int jj = ln & 15;
+          const int tA = 4 * (ln >> 4) + (jj >> 2);
+          const int tB = tA + 16;
+          const int xo = 8 * (jj & 1);
+  #pragma unroll
+          for (int dt = 0; dt < kDimTiles; ++dt) {
+            const int c = 16 * wave + 2 * dt + ((jj >> 1) & 1);
+            const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + slice_off(tA, c) + xo));
+            const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + slice_off(tB, c) + xo));
+            const u32x2 xa = __builtin_bit_cast(u32x2, va);
+            const u32x2 xb = __builtin_bit_cast(u32x2, vb);
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{xa[0], xa[1], xb[0], xb[1]});
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, o[dt], 0, 0, 0);
+          }
         }
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
-      mx = mx == -INFINITY ? -INFINITY : mx * sc;
-      const bool raise = mx > m_run + kRescaleSlack;
-      if (__any(raise)) {
-        const float m_new = raise ? mx : m_run;
-        const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-        m_run = m_new;
-        l_part *= alpha;
-#pragma unroll
-        for (int d = 0; d < kDimTiles; ++d) o[d] *= alpha;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float e[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) e[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -m_use));
-      if (!full) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) e[i] = ((okbits >> i) & 1u) ? e[i] : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) l_part += e[i];
-      // ---- O^T += V^T P^T over the two halves of the page.  PV k-step h
-      // covers key tiles 2 h and 2 h + 1: k-slot i of lane group g is key
-      // 4 g + i of tile 2 h (i < 4) or of tile 2 h + 1 (i >= 4); the
-      // transposed read of 16-lane group G takes keys 4 G + (j >> 2) (+ 16
-      // for the second read) and dims 4 (j & 3) .. + 3 of the dim tile, i.e.
-      // chunk 16 wave + 2 dt + ((j >> 1) & 1) of the half.
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // FP8: wave w's V dims are NoPE group w; the probabilities times
-        // that group's scale of their key (page key 32 h + 16 (i >> 2) +
-        // 4 g + (i & 3) for e[8 h + i]).
-        float ev[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ev[i] = e[8 * h + i];
-          if constexpr (FMT == 1)
-            ev[i] *= *(const float*)(rcur + (32 * h + 16 * (i >> 2) + 4 * g + (i & 3)) * kFp8RowBytes +
-                                     kFp8ScaleOff + 4 * wave);
+      // ---- page j's slot is free once every wave is past its PV: page
+      // j + 2 goes into it now, so that it flies while page j + 1 is awaited.
+      if (j + 2 < je) {
+        lds_barrier();
+        if (SPARSE) {
+          const int pos = kPage * (j + 2);
+          if (pos + kPage - tab_base > G::kTabN) {   // the unit's range outgrew the table
+            tab_base = pos;
+            fill_table<kThreads, G::kTabN / kThreads>(p, tab, b, tab_base, min(pos_end - tab_base, G::kTabN), Wunit, idx_row);
+            wait_vmem<0>();
+            lds_barrier();
+          }
         }
-        const bf16x8 pb = __builtin_bit_cast(
-            bf16x8, u32x4{pack_bf16x2(ev[0], ev[1]), pack_bf16x2(ev[2], ev[3]), pack_bf16x2(ev[4], ev[5]),
-                          pack_bf16x2(ev[6], ev[7])});
-        const uint8_t* vh = kb + h * kSliceBytes;
-        const int ln = opaque_lane();
-        const int jj = ln & 15;
-        const int tA = 4 * (ln >> 4) + (jj >> 2);
-        const int tB = tA + 16;
-        const int xo = 8 * (jj & 1);
-#pragma unroll
-        for (int dt = 0; dt < kDimTiles; ++dt) {
-          const int c = 16 * wave + 2 * dt + ((jj >> 1) & 1);
-          const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + slice_off(tA, c) + xo));
-          const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + slice_off(tB, c) + xo));
-          const u32x2 xa = __builtin_bit_cast(u32x2, va);
-          const u32x2 xb = __builtin_bit_cast(u32x2, vb);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{xa[0], xa[1], xb[0], xb[1]});
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, o[dt], 0, 0, 0);
-        }
+        vis[C] = copy_page<FMT, SPARSE>(p, tab, tab_base, rcur, j + 2, L, page_at(j + 2));
       }
     };
     int j = jb;
