@@ -250,17 +250,17 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
             // scale of their key (the lane's output keys 16 (wave & 1) + 4 g
             // + i of half wave >> 1: raw rows 32 (wave >> 1) + ...).
             f32x4 sc4[4];
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) sc4[i] = fp8_scales(rcur, 32 * (wave >> 1) + 16 * (wave & 1) + 4 * gg + i);
             f32x4 sr = f32x4{0.f, 0.f, 0.f, 0.f};
             sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kh + slice_off(t, 64 + gg)), qf[16], sr,
                                                          0, 0, 0);
             sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(kh + slice_off(t, 68 + gg)), qf[17], sr,
                                                          0, 0, 0);
-  #pragma unroll
+#pragma unroll
             for (int G = 0; G < 4; ++G) {
               f32x4 ta = f32x4{0.f, 0.f, 0.f, 0.f}, tb = ta;
-  #pragma unroll
+#pragma unroll
               for (int kk = 0; kk < 4; kk += 2) {
                 const int ks = 4 * G + kk;
                 const bf16x8 a0 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + gg));
@@ -269,13 +269,13 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
                 tb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks + 1], tb, 0, 0, 0);
               }
               const f32x4 tg = ta + tb;
-  #pragma unroll
+#pragma unroll
               for (int i = 0; i < 4; ++i) sr[i] = __builtin_fmaf(tg[i], sc4[i][G], sr[i]);
             }
             sres = sr;
           } else {
             f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
-  #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < kKSteps; ks += 2) {
               const bf16x8 a0 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + gg));
               const bf16x8 a1 = *(const bf16x8*)(kh + slice_off(t, 4 * ks + 4 + gg));
@@ -289,10 +289,10 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
         lds_barrier();   // all four S^T tiles visible
         // ---- lane holds row l % 16 and keys 16 w + 4 g + i (i < 4) for w < 4.
         float sv[16];
-  #pragma unroll
+#pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           const f32x4 a = *(const f32x4*)(xs + w * 1024 + lane * 16);
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) sv[4 * w + i] = a[i];
         }
         // ---- mask + online softmax (exp2 domain, logit = sc * s).
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
         uint32_t okbits = 0xFFFFu;
         if (!full) {
           okbits = 0u;
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int tl = 16 * (i >> 2) + 4 * g + (i & 3);
             const bool ok = SPARSE ? ((vmask >> tl) & 1u) != 0u : (key0 + tl < W);
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
           }
         }
         float mx = -INFINITY;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[i]);
         mx = fmaxf(mx, xor16(mx));
         mx = fmaxf(mx, xor32(mx));
@@ -321,18 +321,18 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
           const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
           m_run = m_new;
           l_part *= alpha;
-  #pragma unroll
+#pragma unroll
           for (int d = 0; d < kDimTiles; ++d) o[d] *= alpha;
         }
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float e[16];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) e[i] = fast_exp2(__builtin_fmaf(sv[i], sc, -m_use));
         if (!full) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i) e[i] = ((okbits >> i) & 1u) ? e[i] : 0.f;
         }
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) l_part += e[i];
         // ---- O^T += V^T P^T over the two halves of the page.  PV k-step h
         // covers key tiles 2 h and 2 h + 1: k-slot i of lane group g is key
@@ -340,13 +340,13 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
         // transposed read of 16-lane group G takes keys 4 G + (j >> 2) (+ 16
         // for the second read) and dims 4 (j & 3) .. + 3 of the dim tile, i.e.
         // chunk 16 wave + 2 dt + ((j >> 1) & 1) of the half.
-  #pragma unroll
+#pragma unroll
         for (int h = 0; h < 2; ++h) {
           // FP8: wave w's V dims are NoPE group w; the probabilities times
           // that group's scale of their key (page key 32 h + 16 (i >> 2) +
           // 4 g + (i & 3) for e[8 h + i]).
           float ev[8];
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 8; ++i) {
             ev[i] = e[8 * h + i];
             if constexpr (FMT == 1)
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void narrow_kernel(const DecodeParams 
           const int tA = 4 * (ln >> 4) + (jj >> 2);
           const int tB = tA + 16;
           const int xo = 8 * (jj & 1);
-  #pragma unroll
+#pragma unroll
           for (int dt = 0; dt < kDimTiles; ++dt) {
             const int c = 16 * wave + 2 * dt + ((jj >> 1) & 1);
             const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vh + slice_off(tA, c) + xo));
