@@ -158,31 +158,53 @@ __device__ __forceinline__ void copy_slice_trailing(const DecodeParams& p, uint8
 
 // ---- per-slice pieces shared by both kernels ------------------------------
 
+// Per-lane LDS offsets of the bf16 slice reads of lane ln, packed into one
+// register.  Bits 0..15: the K fragment of QK k-step 0 (key l32, chunk
+// 36 hf + g; left 0 when QK is false).  Bits 16..31: the first V^T read of
+// the PV product (key 4 (l >> 5) + (l & 15) / 4, chunk 32 hf + 2 ((l >> 4)
+// & 1) + ((l >> 1) & 1), plus 8 bytes for odd lanes).  Every other fragment
+// of a slice differs from these by an XOR of the swizzled chunk bits (bits
+// 4..6) and an immediate, because stepping the chunk by 2 or 4 or the key by
+// 8 flips single bits of the swizzled position.  The empty asm keeps the
+// value as computed: with ln = threadIdx.x & 63 outside the slice loop it
+// stays in one register, with opaque_lane() inside the loop it is rebuilt
+// in every slice.
+template <bool QK>
+__device__ __forceinline__ int slice_lane_offsets(int ln, int hf) {
+  const int t = ln & 31;
+  const int qk0 = QK ? t * 128 + (((4 * hf + (ln >> 5)) ^ swz(t)) & 7) * 16 + 4 * kGroupBytes * hf : 0;
+  const int jj = ln & 15;
+  const int tA = 4 * (ln >> 5) + (jj >> 2);
+  const int cl0 = 2 * ((ln >> 4) & 1) + ((jj >> 1) & 1);
+  const int v0 = tA * 128 + ((cl0 ^ swz(tA)) & 7) * 16 + 4 * kGroupBytes * hf + 8 * (jj & 1);
+  int packed = qk0 | (v0 << 16);
+  asm volatile("" : "+v"(packed));
+  return packed;
+}
+
 // Partial S^T = K Q^T over this wave's 288 QK dims.  A = K: lane holds key
 // l32, dims 288 hf + 16 ks + 8 g + 0..7, i.e. chunk c = 36 hf + 2 ks + g of
 // its row, in group c / 8 = (hf ? 4 : 0) + (2 ks + 4 hf) / 8.  The swizzled
-// position within the group repeats every 4 k-steps; four lane offsets carry
-// it, the rest is an immediate.  B = Q^T from registers (k-steps < QR) or
-// from this wave's LDS area.
+// position within the group repeats every 4 k-steps: k-steps 4 i + m read
+// at the k-step-0 offset XOR 32 m (m < 2), or XOR 32 m plus one group for
+// wave half 1 (m >= 2), plus i groups.  B = Q^T from registers (k-steps
+// < QR) or from this wave's LDS area.
 template <int QR>
 __device__ __forceinline__ f32x16 qk_partial(const uint8_t* kb, const bf16x8 (&qf)[QR], const uint8_t* qs_mine,
-                                             int hf) {
+                                             int hf, int lofs) {
   f32x16 s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
   const int ln = opaque_lane();
-  const int t = ln & 31;
-  const int gg = ln >> 5;
-  const int sw = swz(t);
-  int ko[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-    ko[m] = t * 128 + (((4 * hf + 2 * m + gg) ^ sw) & 7) * 16 + hf * kGroupBytes * (4 + (m >= 2 ? 1 : 0));
+  int a = lofs & 0xFFFF;
+  asm volatile("" : "+v"(a));   // the four offsets below are formed here, not kept live
+  const uint8_t* const kp[4] = {kb + a, kb + (a ^ 32), kb + (a ^ 64) + hf * kGroupBytes,
+                                kb + (a ^ 96) + hf * kGroupBytes};
   // Three fragment reads stay ahead of the MFMA chain.  The order is pinned
   // with scheduling barriers: left to itself the scheduler moves each read
   // next to its MFMA when the kernel is near its register limit, and every
   // MFMA then waits out a whole LDS round trip.
-  auto frag = [&](int ks) -> bf16x8 { return *(const bf16x8*)(kb + ko[ks & 3] + kGroupBytes * (ks >> 2)); };
+  auto frag = [&](int ks) -> bf16x8 { return *(const bf16x8*)(kp[ks & 3] + kGroupBytes * (ks >> 2)); };
   bf16x8 a0 = frag(0), a1 = frag(1), a2 = frag(2);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -455,7 +477,7 @@ __device__ __forceinline__ void xchg_add(const uint8_t* xs_peer, f32x16& s, int 
 template <bool SPARSE>
 __device__ __forceinline__ void softmax_pv(f32x16& s, f32x16 (&o)[kDimTiles], float& m_run, float& l_part,
                                            const uint8_t* kb, uint32_t vmask, bool full, int W, int key0,
-                                           float sc, int hf, int g) {
+                                           float sc, int hf, int g, int lofs) {
   uint32_t okbits = 0xFFFFu;   // bit r: key of register r visible to this row
   if (!full) {
     const uint32_t lmask = vmask >> (4 * g);   // sparse: bit 8 (r >> 2) + (r & 3)
@@ -509,25 +531,21 @@ __device__ __forceinline__ void softmax_pv(f32x16& s, f32x16 (&o)[kDimTiles], fl
   // (j >> 2) (+ 8 for the second read) and dims 4 (j & 3) .. +3 of the
   // group's 16-dim run 256 hf + 32 dt + 16 (G & 1), i.e. chunk
   // 32 hf + 4 dt + 2 (G & 1) + ((j >> 1) & 1), in group 4 hf + dt / 2.
-  const int ln = opaque_lane();
-  const int jj = ln & 15;
-  const int gb = (ln >> 4) & 1;
-  const int tA = 4 * (ln >> 5) + (jj >> 2);
-  const int tB = tA + 8;
-  const int sA = swz(tA), sB = swz(tB);
-  const int cl0 = 2 * gb + ((jj >> 1) & 1);   // chunk within its group of 8, even dt
-  const int lo = 4 * kGroupBytes * hf + 8 * (jj & 1);
-  const int vA0 = tA * 128 + ((cl0 ^ sA) & 7) * 16 + lo;
-  const int vA1 = tA * 128 + (((cl0 + 4) ^ sA) & 7) * 16 + lo;
-  const int vB0 = tB * 128 + ((cl0 ^ sB) & 7) * 16 + lo;
-  const int vB1 = tB * 128 + (((cl0 + 4) ^ sB) & 7) * 16 + lo;
+  // Odd dt moves the chunk by 4 (XOR 64 on the swizzled offset); the
+  // second read's key + 8 moves 1024 bytes and flips swizzle bit 0 (XOR 16).
+  int v0 = lofs >> 16;
+  asm volatile("" : "+v"(v0));   // as in qk_partial
+  const uint8_t* const pA0 = kb + v0;
+  const uint8_t* const pA1 = kb + (v0 ^ 64);
+  const uint8_t* const pB0 = kb + (v0 ^ 16) + 1024;
+  const uint8_t* const pB1 = kb + (v0 ^ 80) + 1024;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int dt = 0; dt < kDimTiles; ++dt) {
       const int imm = kk * 16 * 128 + kGroupBytes * (dt >> 1);
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + ((dt & 1) ? vA1 : vA0) + imm));
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + ((dt & 1) ? vB1 : vB0) + imm));
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(((dt & 1) ? pA1 : pA0) + imm));
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(((dt & 1) ? pB1 : pB0) + imm));
       const u32x2 xa = __builtin_bit_cast(u32x2, va);
       const u32x2 xb = __builtin_bit_cast(u32x2, vb);
       const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{xa[0], xa[1], xb[0], xb[1]});
@@ -682,6 +700,12 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
   const int g = lane >> 5;
   Item it;
   if (!decode_item(p, it)) return;
+  // The packed slice-read offsets stay in a register for the whole kernel,
+  // except in the exact dense FP8 variant, which is at its register limit
+  // and rebuilds them in every slice (measured: holding them there spills
+  // inside the slice loop and costs 10 %).
+  constexpr bool kLofsHeld = !(FMT == 1 && !SPARSE && QLO);
+  const int lofs_held = kLofsHeld ? slice_lane_offsets<FMT == 0>(lane, hf) : 0;
   const int row_base = it.rt * kRowsPerWg + pr * kRowsPerPair;   // uniform
   const int my_row = row_base + l32;
   const bool row_ok = my_row < p.R;
@@ -776,6 +800,7 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
       ++sl;
       if (vmask == 0u) return;   // no visible key in this slice (uniform)
       const uint8_t* kb = rcur;
+      const int lofs = kLofsHeld ? lofs_held : slice_lane_offsets<FMT == 0>(opaque_lane(), hf);
       f32x16 s;
       if constexpr (FMT == 1) {
         // QK^T reads the raw slice; V is dequantised into kbf (scaled
@@ -797,13 +822,13 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
         }
         kb = kbf;
       } else {
-        s = qk_partial<QR>(kb, qf, qs_mine, hf);
+        s = qk_partial<QR>(kb, qf, qs_mine, hf, lofs);
       }
       xchg_put(xs_mine, s, lane);
       lds_barrier();
       xchg_add(xs_peer, s, lane);
       const bool full = SPARSE ? (vmask == 0xFFFFFFFFu) : (key0 + kSlice <= W_lo);
-      softmax_pv<SPARSE>(s, o, m_run, l_part, kb, vmask, full, W, key0, sc, hf, g);
+      softmax_pv<SPARSE>(s, o, m_run, l_part, kb, vmask, full, W, key0, sc, hf, g, lofs);
     };
     while (sl < s_end) {
       step(Slot<0>{});
@@ -851,6 +876,7 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
   const int g = lane >> 5;
   Item it;
   if (!decode_item(p, it)) return;
+  const int lofs = slice_lane_offsets<true>(lane, hf);   // held for the whole kernel
   const int row_base = it.rt * kRowsPerWg + pr * kRowsPerPair;   // uniform
   const int my_row = row_base + (lane & 31);
   const bool row_ok = my_row < p.R;
@@ -913,20 +939,17 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
         copy_slice_trailing(p, rfree, sl + 2, L, sl + 2 < s_end, page_pf);
         page_pf = page_of(p, b, min(sl + 3, s_end - 1) >> 1, L);
       }
-      f32x16 s;
-      if (vmask != 0u) {
-        s = qk_partial<QR>(rcur, qf, qs_mine, hf);
-        xchg_put(xs_mine, s, lane);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-      }
+      // QK^T also runs on a slice with no visible key (at most the last
+      // slice of a unit, whose slot then holds stale rows): its scores are
+      // never read, and skipping it would cost a zeroed tile every slice.
+      f32x16 s = qk_partial<QR>(rcur, qf, qs_mine, hf, lofs);
+      xchg_put(xs_mine, s, lane);
       if (grp == 1) wait_vmem<9>();   // slice sl + 1 (issued one step earlier)
       lds_barrier();
       // softmax + PV half-step.
       if (vmask != 0u) {
         xchg_add(xs_peer, s, lane);
-        softmax_pv<false>(s, o, m_run, l_part, rcur, vmask, key0 + kSlice <= W_lo, W, key0, sc, hf, g);
+        softmax_pv<false>(s, o, m_run, l_part, rcur, vmask, key0 + kSlice <= W_lo, W, key0, sc, hf, g, lofs);
       }
       lds_barrier();
       ++sl;
