@@ -140,21 +140,25 @@ __device__ __forceinline__ uint32_t issue_slice(const DecodeParams& p, const int
 
 // The whole bf16 slice sl into `slot` by the four waves of the trailing
 // group (waves 4-7): wave 4 + k issues copy instructions inst = 4 G + k,
-// chunk group G = 0..8 of keys 8 k .. 8 k + 7 (bf16_copy_src), nine per
-// wave (none for an empty pool).
+// chunk group G = 0..8 of keys 8 k .. 8 k + 7 (as bf16_copy_src), nine per
+// wave (none for an empty pool).  The slice's keys are consecutive rows of
+// one page, so the page start is a uniform base and each lane adds its row
+// within the page and its swizzled chunk; keys past the sequence take its
+// last key, an inactive slice row 0 of the pool (as slot_row).
 __device__ __forceinline__ void copy_slice_trailing(const DecodeParams& p, uint8_t* slot, int sl, int L, bool active,
                                                     int page_in) {
   if (p.num_pages == 0) return;
   const int ln = opaque_lane();
   const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
-  const int row = slot_row<false>(nullptr, 0, sl, 8 * k + (ln >> 3), L, active, page_in, 0);
-  const uint8_t* src = bf16_copy_src(p, row, k);
+  const int t = 8 * k + (ln >> 3);
+  const int lim = active ? max(L - 1 - (sl >> 1) * kPage, 0) : 0;   // last row of the page to read
+  const int page = active ? page_in : 0;
+  const int r = min((sl & 1) * kSlice + t, lim);
+  const uint32_t voff = __umul24(r, kBf16RowBytes) + 16 * ((ln & 7) ^ swz(t));
+  const uint8_t* const base = p.kcache + (size_t)page * (kPage * kBf16RowBytes);
 #pragma unroll
-  for (int G = 0; G < kSliceBytes / kGroupBytes; ++G) lds_dma16(src + 128 * G, slot + 1024 * (4 * G + k));
+  for (int G = 0; G < kSliceBytes / kGroupBytes; ++G) lds_dma16_s(base + 128 * G, voff, slot + 1024 * (4 * G + k));
 }
-
-
-
 
 // ---- per-slice pieces shared by both kernels ------------------------------
 

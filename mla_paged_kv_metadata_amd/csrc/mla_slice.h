@@ -52,6 +52,14 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_base) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0));
 }
 
+// As lds_dma16, with the source split into a uniform 64-bit base (SGPRs)
+// and a 32-bit per-lane byte offset (the saddr form): the steps between the
+// instructions of one copy are then scalar adds to the base.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, void* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds_base;
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0));
+}
+
 // Wait until at most N vector-memory operations of this wave are pending
 // (s_waitcnt with expcnt and lgkmcnt left at their no-wait maxima; vmcnt is
 // split over bits 3:0 and 15:14).
