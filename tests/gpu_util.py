@@ -11,10 +11,12 @@ import mla_inputs as gen
 
 # Elementwise bounds: |out - ref| <= ATOL + RTOL * |ref|, |lse - ref| <= LSE_TOL.
 # bf16 KV: the bound the task states.  FP8 KV, against the oracle on the
-# exact stored values (code * scale in fp64): the kernels convert every
-# e4m3 code to bf16 exactly and apply the fp32 group scales after the MFMAs
-# (to each group's partial scores and to the probabilities of each V group),
-# so no product code * scale is rounded and the bf16 bounds apply unchanged.
+# exact stored values (code * scale in fp64): the scores take every e4m3
+# code exactly and the fp32 group scales after the MFMAs, so no product
+# code * scale is rounded there; for PV the 16-row kernel scales the
+# probabilities of each V group and the 128-row kernels round code * scale
+# to bf16, a rounding the bf16 path has anyway (its V is bf16), so the bf16
+# bounds apply unchanged.
 TOL = {
     gen.FMT_BF16: dict(atol=1e-2, rtol=1e-2, lse=1e-3),
     gen.FMT_FP8: dict(atol=1e-2, rtol=1e-2, lse=1e-3),
