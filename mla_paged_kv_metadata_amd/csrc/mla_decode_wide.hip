@@ -123,6 +123,22 @@ __device__ __forceinline__ uint32_t issue_slice(const DecodeParams& p, const int
     }
   } else {
     constexpr int kCpr = kFp8RowBytes / 16;   // 41 chunks per row
+    if (!SPARSE && active && (sl + 1) * kSlice <= L) {
+      // Every key of the slice is in the sequence: its 32 rows are
+      // consecutive in one page, and chunk q of the slice (row q / 41,
+      // chunk q % 41) sits at byte 16 q of that run, so the copy is linear:
+      // instruction inst moves bytes 1024 inst .. + 1023 from a uniform
+      // base; lanes past the slice's end re-read its last chunk.
+      const uint8_t* const base = p.kcache + ((size_t)page_in * kPage + (sl & 1) * kSlice) * kFp8RowBytes;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        int inst = wave + kWaves * i;
+        if (inst >= kInst) inst = wave;
+        const uint32_t voff = (uint32_t)min(inst * 1024 + 16 * ln, kSlice * kFp8RowBytes - 16);
+        lds_dma16_s(base, voff, dst + inst * 1024);
+      }
+      return mask;
+    }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       int inst = wave + kWaves * i;
