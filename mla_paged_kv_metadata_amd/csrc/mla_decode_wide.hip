@@ -494,7 +494,9 @@ __device__ __forceinline__ void xchg_add(const uint8_t* xs_peer, f32x16& s, int 
 // masked (full == false).  The reference max m_run is only raised when a
 // row's max exceeds it by more than kRescaleSlack: P then stays below
 // 2^kRescaleSlack and O and the row sum always share one reference.
-template <bool SPARSE>
+// AHEAD V^T fragments are read ahead of the PV MFMAs (measured: 3 in the
+// lock-step kernel, 2 in offset_kernel, where a third was not faster).
+template <bool SPARSE, int AHEAD>
 __device__ __forceinline__ void softmax_pv(f32x16& s, f32x16 (&o)[kDimTiles], float& m_run, float& l_part,
                                            const uint8_t* kb, uint32_t vmask, bool full, int W, int key0,
                                            float sc, int hf, int g, int lofs) {
@@ -559,26 +561,31 @@ __device__ __forceinline__ void softmax_pv(f32x16& s, f32x16 (&o)[kDimTiles], fl
   const uint8_t* const pA1 = kb + (v0 ^ 64);
   const uint8_t* const pB0 = kb + (v0 ^ 16) + 1024;
   const uint8_t* const pB1 = kb + (v0 ^ 80) + 1024;
+  // MFMA i = 8 kk + dt reads its V^T fragment AHEAD MFMAs earlier; the
+  // order is pinned with scheduling barriers (as in qk_partial): left to
+  // the scheduler, the lock-step kernels kept fewer reads in flight.
+  auto vfrag = [&](int i) -> bf16x8 {
+    const int kk = i / kDimTiles, dt = i % kDimTiles;
+    const int imm = kk * 16 * 128 + kGroupBytes * (dt >> 1);
+    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(((dt & 1) ? pA1 : pA0) + imm));
+    const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(((dt & 1) ? pB1 : pB0) + imm));
+    const u32x2 xa = __builtin_bit_cast(u32x2, va);
+    const u32x2 xb = __builtin_bit_cast(u32x2, vb);
+    return __builtin_bit_cast(bf16x8, u32x4{xa[0], xa[1], xb[0], xb[1]});
+  };
+  bf16x8 f[AHEAD];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+  for (int j = 0; j < AHEAD; ++j) f[j] = vfrag(j);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int dt = 0; dt < kDimTiles; ++dt) {
-      const int imm = kk * 16 * 128 + kGroupBytes * (dt >> 1);
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(((dt & 1) ? pA1 : pA0) + imm));
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(((dt & 1) ? pB1 : pB0) + imm));
-      const u32x2 xa = __builtin_bit_cast(u32x2, va);
-      const u32x2 xb = __builtin_bit_cast(u32x2, vb);
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{xa[0], xa[1], xb[0], xb[1]});
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kk], o[dt], 0, 0, 0);
-    }
-  // Keep the reads of two fragments ahead of the MFMAs.
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  for (int i = 0; i < 2 * kDimTiles; ++i) {
+    const int kk = i / kDimTiles, dt = i % kDimTiles;
+    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], pb[kk], o[dt], 0, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 2 * kDimTiles - 2; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int j = 0; j + 1 < AHEAD; ++j) f[j] = f[j + 1];
+    if (i + AHEAD < 2 * kDimTiles) f[AHEAD - 1] = vfrag(i + AHEAD);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 }
 
 // Per-unit setup shared by both kernels: loads this wave's Q^T (k-steps
@@ -848,7 +855,7 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
       lds_barrier();
       xchg_add(xs_peer, s, lane);
       const bool full = SPARSE ? (vmask == 0xFFFFFFFFu) : (key0 + kSlice <= W_lo);
-      softmax_pv<SPARSE>(s, o, m_run, l_part, kb, vmask, full, W, key0, sc, hf, g, lofs);
+      softmax_pv<SPARSE, 3>(s, o, m_run, l_part, kb, vmask, full, W, key0, sc, hf, g, lofs);
     };
     while (sl < s_end) {
       step(Slot<0>{});
@@ -969,7 +976,7 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
       // softmax + PV half-step.
       if (vmask != 0u) {
         xchg_add(xs_peer, s, lane);
-        softmax_pv<false>(s, o, m_run, l_part, rcur, vmask, key0 + kSlice <= W_lo, W, key0, sc, hf, g, lofs);
+        softmax_pv<false, 2>(s, o, m_run, l_part, rcur, vmask, key0 + kSlice <= W_lo, W, key0, sc, hf, g, lofs);
       }
       lds_barrier();
       ++sl;
