@@ -157,23 +157,44 @@ __device__ __forceinline__ uint32_t issue_slice(const DecodeParams& p, const int
 // The whole bf16 slice sl into `slot` by the four waves of the trailing
 // group (waves 4-7): wave 4 + k issues copy instructions inst = 4 G + k,
 // chunk group G = 0..8 of keys 8 k .. 8 k + 7 (as bf16_copy_src), nine per
-// wave (none for an empty pool).  The slice's keys are consecutive rows of
-// one page, so the page start is a uniform base and each lane adds its row
-// within the page and its swizzled chunk; keys past the sequence take its
-// last key, an inactive slice row 0 of the pool (as slot_row).
-__device__ __forceinline__ void copy_slice_trailing(const DecodeParams& p, uint8_t* slot, int sl, int L, bool active,
-                                                    int page_in) {
-  if (p.num_pages == 0) return;
+// wave.  The slice's keys are consecutive rows of one page, so the page
+// start is a uniform base and each lane adds its row within the page and
+// its swizzled chunk; keys past the sequence take its last key, an inactive
+// slice row 0 of the pool (as slot_row).  prep_slice_copy forms the
+// addresses once; issue(G) sends instruction G, so that the nine can be
+// spread between other instructions (the QK MFMAs).  Callers skip the copy
+// for an empty pool.
+struct SliceCopy {
+  const uint8_t* base;
+  uint32_t voff;
+  uint8_t* slot;
+  int k;
+  __device__ __forceinline__ void issue(int G) const { lds_dma16_s(base + 128 * G, voff, slot + 1024 * (4 * G + k)); }
+};
+constexpr int kCopyInst = kSliceBytes / kGroupBytes;   // 9 per wave
+
+__device__ __forceinline__ SliceCopy prep_slice_copy(const DecodeParams& p, uint8_t* slot, int sl, int L, bool active,
+                                                     int page_in) {
   const int ln = opaque_lane();
   const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3;
   const int t = 8 * k + (ln >> 3);
   const int lim = active ? max(L - 1 - (sl >> 1) * kPage, 0) : 0;   // last row of the page to read
   const int page = active ? page_in : 0;
   const int r = min((sl & 1) * kSlice + t, lim);
-  const uint32_t voff = __umul24(r, kBf16RowBytes) + 16 * ((ln & 7) ^ swz(t));
-  const uint8_t* const base = p.kcache + (size_t)page * (kPage * kBf16RowBytes);
+  SliceCopy c;
+  c.voff = __umul24(r, kBf16RowBytes) + 16 * ((ln & 7) ^ swz(t));
+  c.base = p.kcache + (size_t)page * (kPage * kBf16RowBytes);
+  c.slot = slot;
+  c.k = k;
+  return c;
+}
+
+__device__ __forceinline__ void copy_slice_trailing(const DecodeParams& p, uint8_t* slot, int sl, int L, bool active,
+                                                    int page_in) {
+  if (p.num_pages == 0) return;
+  const SliceCopy c = prep_slice_copy(p, slot, sl, L, active, page_in);
 #pragma unroll
-  for (int G = 0; G < kSliceBytes / kGroupBytes; ++G) lds_dma16_s(base + 128 * G, voff, slot + 1024 * (4 * G + k));
+  for (int G = 0; G < kCopyInst; ++G) c.issue(G);
 }
 
 // ---- per-slice pieces shared by both kernels ------------------------------
@@ -208,10 +229,12 @@ __device__ __forceinline__ int slice_lane_offsets(int ln, int hf) {
 // position within the group repeats every 4 k-steps: k-steps 4 i + m read
 // at the k-step-0 offset XOR 32 m (m < 2), or XOR 32 m plus one group for
 // wave half 1 (m >= 2), plus i groups.  B = Q^T from registers (k-steps
-// < QR) or from this wave's LDS area.
-template <int QR>
+// < QR) or from this wave's LDS area.  With COPY the wave also issues the
+// nine instructions of slice copy cp, one after each of the first nine
+// MFMAs, where their issue time is hidden behind the chain.
+template <int QR, bool COPY = false>
 __device__ __forceinline__ f32x16 qk_partial(const uint8_t* kb, const bf16x8 (&qf)[QR], const uint8_t* qs_mine,
-                                             int hf, int lofs) {
+                                             int hf, int lofs, const SliceCopy& cp = SliceCopy{}) {
   f32x16 s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -238,6 +261,7 @@ __device__ __forceinline__ f32x16 qk_partial(const uint8_t* kb, const bf16x8 (&q
     a0 = a1;
     a1 = a2;
     if (ks + 3 < kKSteps) a2 = frag(ks + 3);
+    if (COPY && ks < kCopyInst) cp.issue(ks);
     __builtin_amdgcn_sched_barrier(0);
   }
   return s;
@@ -877,14 +901,16 @@ __global__ __launch_bounds__(kThreads, 1) void wide_kernel(const DecodeParams p)
 // k / 2 (k even) or the softmax + PV half of slice (k - 1) / 2 (k odd), and
 // group 1 the same one half-step later, so that one group's VALU softmax
 // overlaps the other's MFMAs.  Slice s is read in half-steps 2 s .. 2 s + 2.
-// Group 1 issues every copy: at the start of its QK half of slice s
-// (half-step 2 s + 1) it copies slice s + 2 into the slot of slice s - 1
-// (last read in half-step 2 s), nine instructions per wave, and at the end
-// of that half-step it waits for slice s + 1 (issued one step earlier),
-// which group 0 reads next.  The copy issue, which can stall while the
-// compute unit's misses are in flight, thus stays off the softmax group's
-// critical path (measured: MTP and dense prefill 2 % faster than with each
-// group issuing its share at the end of its softmax half).
+// Group 1 issues every copy: in its QK half of slice s (half-step 2 s + 1)
+// it copies slice s + 2 into the slot of slice s - 1 (last read in
+// half-step 2 s), nine instructions per wave, one after each of its first
+// nine QK MFMAs, and at the end of that half-step it waits for slice s + 1
+// (issued one step earlier), which group 0 reads next.  The copy issue,
+// which can stall while the compute unit's misses are in flight, thus
+// stays off the softmax group's critical path (measured: MTP and dense
+// prefill 2 % faster than with each group issuing its share at the end of
+// its softmax half) and hides behind the MFMA chain (dense prefill 2 %
+// faster than issuing all nine before the chain).
 __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams p) {
   using G = Geo<0>;
   constexpr int QL = G::QL;
@@ -960,16 +986,20 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
       uint8_t* const rfree = C == 0 ? ring2 : (C == 1 ? ring0 : ring1);   // slot (C + 2) % 3
       const int key0 = sl * kSlice;
       const uint32_t vmask = key0 >= L ? 0u : (key0 + kSlice <= L ? 0xFFFFFFFFu : (1u << (L - key0)) - 1u);
-      // QK half-step.  The trailing group first refills the free slot
-      // (slice sl - 1's, last read in the half-step before) with slice sl + 2.
-      if (grp == 1) {
-        copy_slice_trailing(p, rfree, sl + 2, L, sl + 2 < s_end, page_pf);
-        page_pf = page_of(p, b, min(sl + 3, s_end - 1) >> 1, L);
+      // QK half-step.  The trailing group refills the free slot (slice
+      // sl - 1's, last read in the half-step before) with slice sl + 2,
+      // its copy instructions spread over the QK MFMAs.  QK^T also runs on
+      // a slice with no visible key (at most the last slice of a unit,
+      // whose slot then holds stale rows): its scores are never read, and
+      // skipping it would cost a zeroed tile every slice.
+      f32x16 s;
+      if (grp == 1 && p.num_pages != 0) {
+        const SliceCopy c = prep_slice_copy(p, rfree, sl + 2, L, sl + 2 < s_end, page_pf);
+        s = qk_partial<QR, true>(rcur, qf, qs_mine, hf, lofs, c);
+      } else {
+        s = qk_partial<QR>(rcur, qf, qs_mine, hf, lofs);
       }
-      // QK^T also runs on a slice with no visible key (at most the last
-      // slice of a unit, whose slot then holds stale rows): its scores are
-      // never read, and skipping it would cost a zeroed tile every slice.
-      f32x16 s = qk_partial<QR>(rcur, qf, qs_mine, hf, lofs);
+      if (grp == 1) page_pf = page_of(p, b, min(sl + 3, s_end - 1) >> 1, L);
       xchg_put(xs_mine, s, lane);
       if (grp == 1) wait_vmem<9>();   // slice sl + 1 (issued one step earlier)
       lds_barrier();
