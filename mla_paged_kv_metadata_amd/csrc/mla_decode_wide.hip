@@ -925,7 +925,6 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = wave & 1;
   const int pr = wave >> 1;
-  const int grp = wave >> 2;   // 0 leads, 1 trails by half a slice
   const int g = lane >> 5;
   Item it;
   if (!decode_item(p, it)) return;
@@ -939,90 +938,102 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
   const float sc = fabsf(p.scale_log2);
   const bool qneg = p.scale_log2 < 0.f;
 
-  int L_nx = it.L0, n_nx = it.n0;   // as in wide_kernel
-  for (int u = it.u0; u <= it.u1; ++u) {
-    const int jb = (u == it.u0) ? it.j0 : 0;
-    const int je_part = (u == it.u1) ? it.j1 : n_nx;
-    const int b = u;
-    const int L = L_nx;
-    if (u < it.u1) {
-      n_nx = scalar_ld(it.unit_blocks, u + 1);
-      L_nx = scalar_ld(p.seqlens, u + 1);
-    }
-    const int je = p.causal ? causal_tile_end(p, it.rt, L, jb, je_part) : je_part;
-    const int s_row = row_ok ? my_row / p.h_q : 0;
-    const int W = p.causal ? min(max(L - p.s_q + 1 + s_row, 0), L) : L;
-    const int W_lo = p.causal ? min(max(L - p.s_q + 1, 0), L) : L;
-    const int s_begin = 2 * jb;
-    const int s_end = 2 * je;   // at least s_begin + 2
-    bf16x8 qf[QR];
-    load_q(p, u, row_base, hf, qneg, qf, qs_mine);
-    wait_vmem<0>();
-
-    float m_run = -INFINITY;
-    float l_part = 0.f;
-    f32x16 o[kDimTiles];
-#pragma unroll
-    for (int d = 0; d < kDimTiles; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
-
-    // Slices s_begin and s_begin + 1, both groups' shares.
-    // All copies are issued by the trailing group, at the start of its QK
-    // half-steps, off the softmax group's critical path.
-    if (grp == 1) {
-      copy_slice_trailing(p, ring0, s_begin, L, true, page_of(p, b, s_begin >> 1, L));
-      copy_slice_trailing(p, ring1, s_begin + 1, L, true, page_of(p, b, (s_begin + 1) >> 1, L));
-      wait_vmem<9>();             // slice s_begin (slice s_begin + 1 may fly)
-    }
-    int page_pf = page_of(p, b, min(s_begin + 2, s_end - 1) >> 1, L);
-    lds_barrier();                // slice s_begin is in LDS
-    if (grp == 1) lds_barrier();  // group 1 starts one half-step later
-
-    int sl = s_begin;
-    auto step = [&](auto slot) __attribute__((always_inline)) {
-      constexpr int C = decltype(slot)::value;
-      uint8_t* const rcur = C == 0 ? ring0 : (C == 1 ? ring1 : ring2);
-      uint8_t* const rfree = C == 0 ? ring2 : (C == 1 ? ring0 : ring1);   // slot (C + 2) % 3
-      const int key0 = sl * kSlice;
-      const uint32_t vmask = key0 >= L ? 0u : (key0 + kSlice <= L ? 0xFFFFFFFFu : (1u << (L - key0)) - 1u);
-      // QK half-step.  The trailing group refills the free slot (slice
-      // sl - 1's, last read in the half-step before) with slice sl + 2,
-      // its copy instructions spread over the QK MFMAs.  QK^T also runs on
-      // a slice with no visible key (at most the last slice of a unit,
-      // whose slot then holds stale rows): its scores are never read, and
-      // skipping it would cost a zeroed tile every slice.
-      f32x16 s;
-      if (grp == 1 && p.num_pages != 0) {
-        const SliceCopy c = prep_slice_copy(p, rfree, sl + 2, L, sl + 2 < s_end, page_pf);
-        s = qk_partial<QR, true>(rcur, qf, qs_mine, hf, lofs, c);
-      } else {
-        s = qk_partial<QR>(rcur, qf, qs_mine, hf, lofs);
+  // Each group runs its own copy of the unit loop, with grp a compile-time
+  // constant: the register allocator then handles the two groups' half-steps
+  // separately instead of merging them at every branch on the group
+  // (measured: MTP and dense prefill split-KV 1.4-1.6 % faster than one
+  // shared loop with run-time branches, same instructions per group).
+  auto units = [&](auto grp_c) __attribute__((always_inline)) {
+    constexpr int grp = decltype(grp_c)::value;   // 0 leads, 1 trails by half a slice
+    int L_nx = it.L0, n_nx = it.n0;   // as in wide_kernel
+    for (int u = it.u0; u <= it.u1; ++u) {
+      const int jb = (u == it.u0) ? it.j0 : 0;
+      const int je_part = (u == it.u1) ? it.j1 : n_nx;
+      const int b = u;
+      const int L = L_nx;
+      if (u < it.u1) {
+        n_nx = scalar_ld(it.unit_blocks, u + 1);
+        L_nx = scalar_ld(p.seqlens, u + 1);
       }
-      if (grp == 1) page_pf = page_of(p, b, min(sl + 3, s_end - 1) >> 1, L);
-      xchg_put(xs_mine, s, lane);
-      if (grp == 1) wait_vmem<9>();   // slice sl + 1 (issued one step earlier)
-      lds_barrier();
-      // softmax + PV half-step.
-      if (vmask != 0u) {
-        xchg_add(xs_peer, s, lane);
-        softmax_pv<false, 2>(s, o, m_run, l_part, rcur, vmask, key0 + kSlice <= W_lo, W, key0, sc, hf, g, lofs);
+      const int je = p.causal ? causal_tile_end(p, it.rt, L, jb, je_part) : je_part;
+      const int s_row = row_ok ? my_row / p.h_q : 0;
+      const int W = p.causal ? min(max(L - p.s_q + 1 + s_row, 0), L) : L;
+      const int W_lo = p.causal ? min(max(L - p.s_q + 1, 0), L) : L;
+      const int s_begin = 2 * jb;
+      const int s_end = 2 * je;   // at least s_begin + 2
+      bf16x8 qf[QR];
+      load_q(p, u, row_base, hf, qneg, qf, qs_mine);
+      wait_vmem<0>();
+
+      float m_run = -INFINITY;
+      float l_part = 0.f;
+      f32x16 o[kDimTiles];
+  #pragma unroll
+      for (int d = 0; d < kDimTiles; ++d)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+
+      // Slices s_begin and s_begin + 1, both groups' shares.
+      // All copies are issued by the trailing group, at the start of its QK
+      // half-steps, off the softmax group's critical path.
+      if (grp == 1) {
+        copy_slice_trailing(p, ring0, s_begin, L, true, page_of(p, b, s_begin >> 1, L));
+        copy_slice_trailing(p, ring1, s_begin + 1, L, true, page_of(p, b, (s_begin + 1) >> 1, L));
+        wait_vmem<9>();             // slice s_begin (slice s_begin + 1 may fly)
       }
-      lds_barrier();
-      ++sl;
-    };
-    while (sl < s_end) {
-      step(Slot<0>{});
-      if (sl >= s_end) break;
-      step(Slot<1>{});
-      if (sl >= s_end) break;
-      step(Slot<2>{});
+      int page_pf = page_of(p, b, min(s_begin + 2, s_end - 1) >> 1, L);
+      lds_barrier();                // slice s_begin is in LDS
+      if (grp == 1) lds_barrier();  // group 1 starts one half-step later
+
+      int sl = s_begin;
+      auto step = [&](auto slot) __attribute__((always_inline)) {
+        constexpr int C = decltype(slot)::value;
+        uint8_t* const rcur = C == 0 ? ring0 : (C == 1 ? ring1 : ring2);
+        uint8_t* const rfree = C == 0 ? ring2 : (C == 1 ? ring0 : ring1);   // slot (C + 2) % 3
+        const int key0 = sl * kSlice;
+        const uint32_t vmask = key0 >= L ? 0u : (key0 + kSlice <= L ? 0xFFFFFFFFu : (1u << (L - key0)) - 1u);
+        // QK half-step.  The trailing group refills the free slot (slice
+        // sl - 1's, last read in the half-step before) with slice sl + 2,
+        // its copy instructions spread over the QK MFMAs.  QK^T also runs on
+        // a slice with no visible key (at most the last slice of a unit,
+        // whose slot then holds stale rows): its scores are never read, and
+        // skipping it would cost a zeroed tile every slice.
+        f32x16 s;
+        if (grp == 1 && p.num_pages != 0) {
+          const SliceCopy c = prep_slice_copy(p, rfree, sl + 2, L, sl + 2 < s_end, page_pf);
+          s = qk_partial<QR, true>(rcur, qf, qs_mine, hf, lofs, c);
+        } else {
+          s = qk_partial<QR>(rcur, qf, qs_mine, hf, lofs);
+        }
+        if (grp == 1) page_pf = page_of(p, b, min(sl + 3, s_end - 1) >> 1, L);
+        xchg_put(xs_mine, s, lane);
+        if (grp == 1) wait_vmem<9>();   // slice sl + 1 (issued one step earlier)
+        lds_barrier();
+        // softmax + PV half-step.
+        if (vmask != 0u) {
+          xchg_add(xs_peer, s, lane);
+          softmax_pv<false, 2>(s, o, m_run, l_part, rcur, vmask, key0 + kSlice <= W_lo, W, key0, sc, hf, g, lofs);
+        }
+        lds_barrier();
+        ++sl;
+      };
+      while (sl < s_end) {
+        step(Slot<0>{});
+        if (sl >= s_end) break;
+        step(Slot<1>{});
+        if (sl >= s_end) break;
+        step(Slot<2>{});
+      }
+      if (grp == 0) lds_barrier();   // group 0 sits out group 1's last half-step
+      store_unit(p, o, m_run, l_part + xor32(l_part), u, it.u0, it.split0, row_base, hf);
+      wait_vmem<0>();
+      lds_barrier();   // the next unit reuses the ring
     }
-    if (grp == 0) lds_barrier();   // group 0 sits out group 1's last half-step
-    store_unit(p, o, m_run, l_part + xor32(l_part), u, it.u0, it.split0, row_base, hf);
-    wait_vmem<0>();
-    lds_barrier();   // the next unit reuses the ring
-  }
+  };
+  if (wave >> 2)
+    units(Slot<1>{});
+  else
+    units(Slot<0>{});
 }
 
 }  // namespace wide
