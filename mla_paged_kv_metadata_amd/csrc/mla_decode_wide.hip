@@ -968,9 +968,9 @@ __global__ __launch_bounds__(kThreads, 1) void offset_kernel(const DecodeParams 
       float m_run = -INFINITY;
       float l_part = 0.f;
       f32x16 o[kDimTiles];
-  #pragma unroll
+#pragma unroll
       for (int d = 0; d < kDimTiles; ++d)
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
 
       // Slices s_begin and s_begin + 1, both groups' shares.
