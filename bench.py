@@ -35,8 +35,9 @@ Every graph's output is checked bit for bit against an eager call first.
 committed counter summary in profiles/ when it was taken on the kernel
 sources as they are now, else null.  `sclk_mhz` is the shader clock sampled
 while the MTP graphs run; `hbm_copy_gbs` is the rate of a plain 1 GiB
-device copy (read + write bytes over time), the streaming rate a simple
-kernel reaches on this part.
+device copy (read + write bytes over time) and `hbm_read_gbs` that of a
+plain 1 GiB read (a sum reduction), the streaming rates simple kernels
+reach on this part.
 
     python bench.py --only WORKLOAD --graph-only
 
@@ -524,6 +525,32 @@ def copy_rate(reps: int = 10) -> float:
     return round(rate, 1)
 
 
+def read_rate(reps: int = 10) -> float:
+    """HBM rate of a plain device read (torch's sum over 1 GiB of fp32, a
+    reduction that reads every byte once and writes a scalar), GB/s over
+    `reps` back-to-back reductions timed with HIP events: the read-only
+    stream a simple library kernel reaches, the access pattern closest to
+    the decode's."""
+    import torch
+    n = 256 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        s = src.sum()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        s = src.sum()
+    b.record()
+    torch.cuda.synchronize()
+    if float(s) != float(n):
+        raise RuntimeError("read-rate reduction gave a wrong sum")
+    rate = n * 4 * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, s
+    torch.cuda.empty_cache()
+    return round(rate, 1)
+
+
 def roofline_object(w, t, bound: str) -> dict:
     """Roofline of the dominant kernel: algorithmic bytes (hbm) or flops
     (mfma) per launch over its mean launch duration in the timed graphs."""
@@ -640,6 +667,7 @@ def main():
         "step_with_schedule_kv_gbs": round(kv / (tm["step_with_schedule"]["mean"] * 1e-3) / 1e9, 1),
         "roofline": roofline_object(prim, tm, "hbm"),
         "hbm_copy_gbs": copy_rate(),
+        "hbm_read_gbs": read_rate(),
     }
     if not args.only_primary:
         extra = {}
