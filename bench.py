@@ -35,9 +35,9 @@ Every graph's output is checked bit for bit against an eager call first.
 committed counter summary in profiles/ when it was taken on the kernel
 sources as they are now, else null.  `sclk_mhz` is the shader clock sampled
 while the MTP graphs run; `hbm_copy_gbs` is the rate of a plain 1 GiB
-device copy (read + write bytes over time) and `hbm_read_gbs` that of a
-plain 1 GiB read (a sum reduction), the streaming rates simple kernels
-reach on this part.
+device copy (read + write bytes over time) and `hbm_read` that of a
+plain 1 GiB read (the reference kernel in libmla_bw.so), the streaming
+rates simple kernels reach on this part.
 
     python bench.py --only WORKLOAD --graph-only
 
@@ -525,30 +525,43 @@ def copy_rate(reps: int = 10) -> float:
     return round(rate, 1)
 
 
-def read_rate(reps: int = 10) -> float:
-    """HBM rate of a plain device read (torch's sum over 1 GiB of fp32, a
-    reduction that reads every byte once and writes a scalar), GB/s over
-    `reps` back-to-back reductions timed with HIP events: the read-only
-    stream a simple library kernel reaches, the access pattern closest to
-    the decode's."""
+def read_rate(reps: int = 10) -> dict:
+    """HBM rate of a plain streaming read: the reference kernel of
+    libmla_bw.so (16-byte loads, eight in flight per lane, every byte read
+    once) over 1 GiB, GB/s over `reps` back-to-back launches timed with HIP
+    events, for a few grid sizes; the best is the read rate a simple kernel
+    reaches on this part."""
+    import ctypes
     import torch
-    n = 256 * 1024 * 1024
-    src = torch.ones(n, dtype=torch.float32, device="cuda")
-    for _ in range(2):
-        s = src.sum()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(reps):
-        s = src.sum()
-    b.record()
-    torch.cuda.synchronize()
-    if float(s) != float(n):
-        raise RuntimeError("read-rate reduction gave a wrong sum")
-    rate = n * 4 * reps / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src, s
+    import mla_paged_kv_metadata_amd as m
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(m.__file__), "libmla_bw.so"))
+    lib.mla_bw_read.restype = ctypes.c_int
+    lib.mla_bw_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    grids = (1024, 2048, 4096, 8192)
+    sink = torch.empty(max(grids) * 4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    rates = {}
+    for blocks in grids:
+        def launch():
+            rc = lib.mla_bw_read(src.data_ptr(), nbytes, sink.data_ptr(), blocks, stream)
+            if rc != 0:
+                raise RuntimeError(f"mla_bw_read failed ({rc})")
+        for _ in range(2):
+            launch()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            launch()
+        b.record()
+        torch.cuda.synchronize()
+        rates[blocks] = round(nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    del src, sink
     torch.cuda.empty_cache()
-    return round(rate, 1)
+    best = max(rates, key=rates.get)
+    return {"gbs": rates[best], "workgroups": best, "by_workgroups": rates}
 
 
 def roofline_object(w, t, bound: str) -> dict:
@@ -667,7 +680,7 @@ def main():
         "step_with_schedule_kv_gbs": round(kv / (tm["step_with_schedule"]["mean"] * 1e-3) / 1e9, 1),
         "roofline": roofline_object(prim, tm, "hbm"),
         "hbm_copy_gbs": copy_rate(),
-        "hbm_read_gbs": read_rate(),
+        "hbm_read": read_rate(),
     }
     if not args.only_primary:
         extra = {}

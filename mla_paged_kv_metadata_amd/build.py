@@ -3,7 +3,8 @@
     python -m mla_paged_kv_metadata_amd.build
 
 Each source is compiled to an object in csrc/_build/ (in parallel), then
-linked into mla_paged_kv_metadata_amd/libmla.so.  No GPU is needed to build.
+linked into mla_paged_kv_metadata_amd/libmla.so; the benchmark's
+read-bandwidth reference goes into libmla_bw.so.  No GPU is needed to build.
 """
 from __future__ import annotations
 
@@ -18,6 +19,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmla.so")
+# The benchmark's read-bandwidth reference (not part of the decode ABI).
+LIB_BW = os.path.join(HERE, "libmla_bw.so")
+BW_SOURCE = "hbm_read.hip"
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["mla_api.cpp", "mla_metadata.hip", "mla_decode.hip", "mla_decode_narrow.hip",
@@ -64,7 +68,24 @@ def build(extra=None, verbose: bool = False, out: str = LIB, objdir: str = BUILD
     os.replace(tmp, out)
     if verbose:
         print(f"built {out}")
+    if out == LIB:
+        build_bw(verbose=verbose)
     return out
+
+
+def build_bw(verbose: bool = False) -> str:
+    """Compile the read-bandwidth reference kernel into libmla_bw.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    obj = _compile(BW_SOURCE, [], BUILD)
+    tmp = LIB_BW + ".tmp"
+    r = subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB_BW)
+    if verbose:
+        print(f"built {LIB_BW}")
+    return LIB_BW
 
 
 if __name__ == "__main__":

@@ -204,3 +204,20 @@ def test_fp8_query_option_needs_fp8_pool_and_wide_units(lib, kw, code):
     assert lib.mla_workspace_size(ctypes.byref(a), ctypes.byref(n)) == code
     if code:
         assert b"qk_fp8" in lib.mla_last_error()
+
+
+def test_bandwidth_reference_library_rejects_bad_arguments():
+    # libmla_bw.so: the benchmark's read-bandwidth reference, apart from the
+    # decode ABI.  Bad arguments return -1 before any HIP call.
+    path = os.path.join(ROOT, "mla_paged_kv_metadata_amd", "libmla_bw.so")
+    if not os.path.exists(path):
+        pytest.fail("libmla_bw.so is not built (python -m mla_paged_kv_metadata_amd.build)")
+    bw = ctypes.CDLL(path)
+    bw.mla_bw_read.restype = ctypes.c_int
+    bw.mla_bw_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    fake = ctypes.c_void_p(1 << 20)
+    assert bw.mla_bw_read(None, 32768, fake, 1, None) == -1             # no source
+    assert bw.mla_bw_read(fake, 32768, None, 1, None) == -1             # no sink
+    assert bw.mla_bw_read(fake, 32768, fake, 0, None) == -1             # no workgroups
+    assert bw.mla_bw_read(fake, 32768 + 16, fake, 1, None) == -1        # not whole 32 KiB chunks
+    assert bw.mla_bw_read(ctypes.c_void_p((1 << 20) + 4), 32768, fake, 1, None) == -1   # misaligned
